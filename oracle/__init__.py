@@ -1,0 +1,25 @@
+"""fp64 CPU oracle for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or link
+this package: only the test suite, the smoke check in ``__graft_entry__`` and the
+CPU-baseline leg of ``bench.py`` use it.  It shares no code with the HIP path.
+
+It is the plain, materialising definition of scaled dot-product attention written
+out in numpy float64 (see :mod:`oracle.attention` for the passages each function
+follows), plus the footprint arithmetic of the pages' worked example.
+"""
+from .attention import (
+    attention_fwd,
+    attention_bwd,
+    attention_probs,
+    materialised_bytes,
+    to_f64,
+)
+
+__all__ = [
+    "attention_fwd",
+    "attention_bwd",
+    "attention_probs",
+    "materialised_bytes",
+    "to_f64",
+]

@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs shared by the oracle side and the HIP side.
+
+This module holds no attention arithmetic: it only draws i.i.d. N(0,1) numbers
+from numpy's PCG64 generator in float32 and rounds them to the kernel dtype
+(round-to-nearest-even, through torch's CPU cast).  Both the fp64 oracle and
+the GPU path receive exactly the same bit patterns.
+
+The five workloads are the kernel-level shapes named for this attention path:
+a single-head check, an 8-head d=64 fp16 case with the same shape and dtype as
+the flash-attention-sm75 README's usage example, a bf16 d=128 causal case with
+enlarged queries on half the heads, a grouped-query long-context case, and a
+forward+backward case.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str          # "fp16" | "bf16"
+    causal: tuple       # causal settings run on the same inputs
+    seeds: tuple        # seeds for Q, K, V (and dO)
+    q_boost_heads: int = 0   # Q heads [0, q_boost_heads) multiplied by q_boost (exact power of two)
+    q_boost: float = 1.0
+    backward: bool = False
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), as the fp32 value the kernel receives."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def torch_dtype(self):
+        return {"fp16": torch.float16, "bf16": torch.bfloat16}[self.dtype]
+
+
+WORKLOADS = {
+    "single_head_n256_d64_fp16": Workload(
+        "single_head_n256_d64_fp16", 1, 1, 1, 256, 64, "fp16", (False,), (1000, 1001, 1002),
+        note="single-head forward, oracle finishes in well under a second"),
+    "mha8_n1024_d64_fp16": Workload(
+        "mha8_n1024_d64_fp16", 1, 8, 8, 1024, 64, "fp16", (False, True), (2000, 2001, 2002),
+        note="8-head forward, causal and non-causal on the same inputs"),
+    "b4_h32_n4096_d128_bf16_causal_qx8": Workload(
+        "b4_h32_n4096_d128_bf16_causal_qx8", 4, 32, 32, 4096, 128, "bf16", (True,), (3000, 3001, 3002),
+        q_boost_heads=16, q_boost=8.0,
+        note="Q on heads 0-15 scaled by 8 to force large row maxima"),
+    "gqa_b2_hq32_hkv8_n8192_d128_bf16_causal": Workload(
+        "gqa_b2_hq32_hkv8_n8192_d128_bf16_causal", 2, 32, 8, 8192, 128, "bf16", (True,), (4000, 4001, 4002),
+        note="grouped-query long-context forward; 4 query heads per K/V head"),
+    "fwd_bwd_h16_n4096_d128_bf16_causal": Workload(
+        "fwd_bwd_h16_n4096_d128_bf16_causal", 1, 16, 16, 4096, 128, "bf16", (True,), (5000, 5001, 5002, 5003),
+        backward=True, note="forward then backward with recomputation"),
+}
+
+# The workload the throughput metric is quoted on (N=8192, d=128, bf16, causal).
+HEADLINE = "gqa_b2_hq32_hkv8_n8192_d128_bf16_causal"
+
+
+def randn(seed: int, shape, dtype) -> torch.Tensor:
+    """i.i.d. N(0,1) drawn in float32 from PCG64(seed), rounded (RNE) to `dtype` on the CPU."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=tuple(shape), dtype=np.float32)
+    return torch.from_numpy(x).to(dtype)
+
+
+def make_inputs(w: Workload, N: int | None = None):
+    """CPU tensors (q, k, v[, do]) for workload `w`; `N` overrides the sequence length."""
+    N = w.N if N is None else N
+    dt = w.torch_dtype
+    q = randn(w.seeds[0], (w.B, w.Hq, N, w.d), dt)
+    k = randn(w.seeds[1], (w.B, w.Hkv, N, w.d), dt)
+    v = randn(w.seeds[2], (w.B, w.Hkv, N, w.d), dt)
+    if w.q_boost_heads:
+        q[:, : w.q_boost_heads] *= w.q_boost      # power of two: exact in bf16/fp16
+    out = [q, k, v]
+    if w.backward:
+        out.append(randn(w.seeds[3], (w.B, w.Hq, N, w.d), dt))
+    return tuple(out)
+
+
+def random_case(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype, with_do: bool = False):
+    """Small seeded case for sweeps over shapes (sequence tails, tiny N, GQA/MQA)."""
+    q = randn(seed, (B, Hq, N, d), dtype)
+    k = randn(seed + 1, (B, Hkv, N, d), dtype)
+    v = randn(seed + 2, (B, Hkv, N, d), dtype)
+    if with_do:
+        return q, k, v, randn(seed + 3, (B, Hq, N, d), dtype)
+    return q, k, v
