@@ -1,0 +1,158 @@
+"""Throughput of the attention hot path on one MI355X: fa_fwd + fa_bwd per step.
+
+Workload: the grouped-query long-context case, B=2, Hq=32, Hkv=8, N=8192,
+d=128, bf16, causal (the configuration the metric is quoted on).  A step is one
+forward pass (O and LSE) followed by one backward pass (dQ, dK, dV) over one
+batch of seeded synthetic inputs already resident in HBM.
+
+Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s with the algorithmic FLOP
+count (forward 4*B*Hq*N^2*d, backward 10*B*Hq*N^2*d, both halved for causal).
+`roofline` describes the kernel that takes most of the step; per-pass figures
+are under `passes`.  `cpu_baseline` times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--fwd-only]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fwd-only", action="store_true", help="time only the forward pass (profiling)")
+    p.add_argument("--cpu-heads", type=int, default=12, help="query heads in the CPU-baseline sample")
+    return p.parse_args()
+
+
+def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
+    """The fp64 oracle on one K/V group of the workload: `heads` query heads, all N rows."""
+    import oracle
+    from exact_io_aware_fwd_amd import metrics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    q, k, v, do = inputs
+    G = w.Hq // w.Hkv
+    heads = max(G, min(heads, w.Hq) // G * G)        # whole K/V groups of batch 0
+    qs, ks, vs, dos = q[:1, :heads], k[:1, :heads // G], v[:1, :heads // G], do[:1, :heads]
+    t0 = time.perf_counter()
+    oracle.attention_fwd(qs, ks, vs, True in w.causal, w.scale)
+    flops = metrics.fwd_flops(1, heads, w.N, w.d, True in w.causal)
+    if not fwd_only:
+        oracle.attention_bwd(qs, ks, vs, dos, True in w.causal, w.scale)
+        flops += metrics.bwd_flops(1, heads, w.N, w.d, True in w.causal)
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"batch 0, query heads 0-{heads - 1} with their K/V heads, all {w.N} rows, "
+                  f"{'forward' if fwd_only else 'forward + backward'} in numpy float64 "
+                  f"(materialising, full N^2 even when causal; credited the same algorithmic FLOPs); "
+                  f"{dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import exact_io_aware_fwd_amd as fa
+    from exact_io_aware_fwd_amd import metrics
+
+    w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    causal = True in w.causal
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu_inputs = workloads.make_inputs(w)
+    if len(cpu_inputs) == 3:
+        cpu_inputs = cpu_inputs + (workloads.randn(w.seeds[2] + 1, (w.B, w.Hq, w.N, w.d), w.torch_dtype),)
+    q, k, v, do = (t.to(dev) for t in cpu_inputs)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, q.dtype, causal), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fa.fwd(q, k, v, causal=causal, softmax_scale=w.scale, out=o, lse=lse)
+        if not args.fwd_only:
+            fa.bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=w.scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fa.fwd(q, k, v, causal=causal, softmax_scale=w.scale, out=o, lse=lse)
+        ev[i][1].record(stream)
+        if not args.fwd_only:
+            fa.bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=w.scale, workspace=ws)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    f_fwd = metrics.fwd_flops(w.B, w.Hq, w.N, w.d, causal)
+    f_bwd = 0.0 if args.fwd_only else metrics.bwd_flops(w.B, w.Hq, w.N, w.d, causal)
+    peak = metrics.MFMA_BF16_TFLOPS
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+
+    passes = {"fwd": {"kernel": "fwd_kernel", "launches": 1, "ms": fwd_ms,
+                      "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12}}
+    passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
+    if not args.fwd_only:
+        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_main_kernel + bwd_dq_kernel", "launches": 3,
+                         "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12}
+        passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
+    dom = max(passes, key=lambda n: passes[n]["ms"])
+    roof = {"bound": "mfma", "achieved": passes[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
+            "frac": passes[dom]["frac"], "traffic": None, "kernel": passes[dom]["kernel"],
+            "per_launch_flops": f_fwd if dom == "fwd" else f_bwd, "avg_ms": passes[dom]["ms"]}
+
+    dt_name = {torch.bfloat16: "bf16", torch.float16: "fp16"}[q.dtype]
+    rec = {
+        "metric": "attention fwd/bwd TFLOPS and % MFMA peak at N=8192 d=128 bf16 causal",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dt_name, "data": "synthetic (seeded iid N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": causal, "step": "fa_fwd" if args.fwd_only else "fa_fwd + fa_bwd",
+                   "flops_per_step": f_fwd + f_bwd},
+        "frac_of_peak": value / peak,
+        "roofline": roof,
+        "passes": passes,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_heads, args.fwd_only)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+"""Thin Python binding of the C ABI in include/fa.h (argument marshalling only).
+
+torch supplies device memory and the current stream; every step of the attention
+computation runs in the HIP kernels of libfa.so.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+torch is imported before libfa.so is loaded so that the library binds to the
+HIP runtime torch already has in the process (both carry the same soname).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "fa.h")
+
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F16, FA_BF16 = 0, 1
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by exact_io_aware_fwd_amd.build) and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m exact_io_aware_fwd_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                         ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
+    L.fa_fwd.restype = ctypes.c_int
+    L.fa_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+    L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                         _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_status_string.argtypes = [ctypes.c_int]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 or bfloat16)")
+
+
+def _check(t: torch.Tensor, name: str, device, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, Hkv, N, d] matching q {tuple(q.shape)}; got {tuple(k.shape)}")
+    return B, Hq, k.shape[1], N, d
+
+
+def _raise(st: int):
+    raise FaError(st, last_error())
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        softmax_scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """O, LSE = attention(q, k, v) via fa_fwd on the current stream.
+
+    q [B,Hq,N,d], k/v [B,Hkv,N,d] (fp16 or bf16, contiguous, same device);
+    returns O [B,Hq,N,d] (q's dtype) and LSE [B,Hq,N] float32 (natural log).
+    """
+    L = load()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dev, q.dtype)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(o, "out", dev, q.dtype)
+    _check(lse_t, "lse", dev, torch.float32)
+    if o.shape != q.shape or lse_t.shape != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                      B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return o, lse_t
+
+
+def bwd_workspace_size(B: int, Hq: int, Hkv: int, N: int, d: int, dtype, causal: bool) -> int:
+    code = FA_BF16 if dtype == torch.bfloat16 else FA_F16
+    return int(load().fa_bwd_workspace_size(B, Hq, Hkv, N, d, code, int(bool(causal))))
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None,
+        workspace: torch.Tensor | None = None):
+    """dQ, dK, dV via fa_bwd on the current stream (workspace allocated by torch if not given)."""
+    L = load()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, dev, q.dtype)
+    _check(lse, "lse", dev, torch.float32)
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, Hq, N):
+        raise ValueError("o/do/lse have the wrong shape")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    need = bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype, causal)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _check(ws, "workspace", dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                      B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return dq, dk, dv

@@ -1,0 +1,166 @@
+// C ABI of the attention library: host-side validation, then launches on the
+// caller's stream.  See include/fa.h for the contract of every entry point.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Size checks shared by the forward and backward passes.  Sets *empty when
+// there is nothing to compute (B == 0 or N == 0).
+fa_status check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype,
+                      bool* empty) {
+  if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARGUMENT, "B and N must be >= 0 (B=%lld N=%lld)",
+                                  (long long)B, (long long)N);
+  if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1 (Hq=%lld Hkv=%lld)",
+                                     (long long)Hq, (long long)Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                                 (long long)Hq, (long long)Hkv);
+  if (d < 1) return fail(FA_ERR_INVALID_ARGUMENT, "d must be >= 1 (d=%lld)", (long long)d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                                       (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  // Index arithmetic inside the kernels: per-head offsets are 64-bit; rows,
+  // heads and block counts are 32-bit.
+  if (B > INT_MAX || Hq > INT_MAX || N > INT_MAX / 2 || B * Hq > INT_MAX || N * d > INT_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes exceed the supported index range");
+  const int64_t nqb = (N + 255) / 256;
+  if (B * Hq > 0 && nqb > (int64_t)UINT_MAX / (B * Hq))
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
+  *empty = (B == 0 || N == 0);
+  return FA_OK;
+}
+
+fa_status check_scale(float s) {
+  if (!std::isfinite(s) || !(s > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0 (got %g)", (double)s);
+  return FA_OK;
+}
+
+fa_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype, int causal, float softmax_scale,
+                 struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = check_sizes(B, Hq, Hkv, N, d, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(k, "k")) != FA_OK ||
+      (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
+      (st = check_ptr(lse, "lse")) != FA_OK)
+    return st;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t err = fa::launch_fwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype,
+                             int causal) {
+  (void)causal;
+  bool empty = false;
+  if (check_sizes(B, Hq, Hkv, N, d, dtype, &empty) != FA_OK) return 0;
+  return fa::bwd_dsum_bytes(B, Hq, N) + fa::bwd_dqacc_bytes(B, Hq, N, d);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype, int causal,
+                 float softmax_scale, struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = check_sizes(B, Hq, Hkv, N, d, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(k, "k")) != FA_OK ||
+      (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
+      (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(dout, "dout")) != FA_OK ||
+      (st = check_ptr(dq, "dq")) != FA_OK || (st = check_ptr(dk, "dk")) != FA_OK ||
+      (st = check_ptr(dv, "dv")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
+    return st;
+  const size_t need = fa::bwd_dsum_bytes(B, Hq, N) + fa::bwd_dqacc_bytes(B, Hq, N, d);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                need);
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = static_cast<float*>(workspace);
+  a.dqacc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + fa::bwd_dsum_bytes(B, Hq, N));
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t err = fa::launch_bwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+}  // extern "C"

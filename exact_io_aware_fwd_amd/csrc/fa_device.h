@@ -1,0 +1,91 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// element traits with the 32x32x16 MFMA, packed round-to-nearest-even
+// conversions, the LDS transposing read, and wave-level reductions.
+//
+// MFMA v_mfma_f32_32x32x16_{bf16,f16} lane layout (wave64), checked on the device:
+//   A (32x16):  lane l holds A[l%32][8*(l/32) + 0..7]
+//   B (16x32):  lane l holds B[8*(l/32) + 0..7][l%32]
+//   C (32x32):  lane l holds C[8*(v/4) + 4*(l/32) + v%4][l%32], v = 0..15
+// ds_read_b64_tr_b16: within each 16-lane group, with M[j][c] the four 16-bit
+// elements lane j addresses, lane i receives M[4r + i/4][i%4] for r = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct bf16_tag {};
+struct f16_tag {};
+
+template <class Tag> struct Elt;
+
+template <> struct Elt<bf16_tag> {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two floats -> two bf16 (RNE) in one dword, `lo` in the low half
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    return __uint_as_float(((uint32_t)bits) << 16);
+  }
+};
+
+template <> struct Elt<f16_tag> {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 r = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+};
+
+// 8 contiguous bytes of LDS, read transposed across each 16-lane group.
+static __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+static __device__ __forceinline__ u32x4 cat(u32x2 lo, u32x2 hi) {
+  u32x4 r = {lo.x, lo.y, hi.x, hi.y};
+  return r;
+}
+
+// Reductions across the two half-waves: every lane gets op(x[l], x[l^32]).
+// permlane32_swap(x, x) yields (x[l], x[l+32]) in lanes 0-31 and (x[l-32], x[l]) in 32-63.
+static __device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+static __device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+static constexpr float kLog2e = 1.4426950408889634f;
+static constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace fa

@@ -1,0 +1,50 @@
+// Launch-side interface between the C ABI (fa_api.cpp) and the kernels.
+// Arguments reaching these functions have been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N;
+  float scale;        // softmax scale
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;   // workspace: D_i = sum_k dO_ik O_ik, [B, Hq, N] fp32
+  float* dqacc;  // workspace: dQ accumulator (unscaled), [B, Hq, N, d] fp32
+  int B, Hq, Hkv, N;
+  float scale;
+  float scale_log2;
+};
+
+// Return a hipError_t from the launches (hipSuccess when all were enqueued).
+hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+
+// Workspace layout of the backward pass (bytes, each part 256-byte aligned).
+inline size_t bwd_dsum_bytes(int64_t B, int64_t Hq, int64_t N) {
+  return (size_t)((B * Hq * N * 4 + 255) / 256 * 256);
+}
+inline size_t bwd_dqacc_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
+  return (size_t)((B * Hq * N * d * 4 + 255) / 256 * 256);
+}
+
+}  // namespace fa

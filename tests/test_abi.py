@@ -1,0 +1,108 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/fa.h
+declares, and rejects invalid arguments on the host before any HIP call.
+
+Every call below fails validation (or has nothing to compute), so nothing is
+launched; the pointer values are never dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+from exact_io_aware_fwd_amd import binding
+
+OK, INV, UNS = binding.FA_OK, binding.FA_ERR_INVALID_ARGUMENT, binding.FA_ERR_UNSUPPORTED
+P = 0x10000          # an aligned fake device address (never dereferenced here)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = binding.declared_symbols()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_status_strings(L):
+    assert binding.status_string(OK) == "FA_OK"
+    assert binding.status_string(INV) == "FA_ERR_INVALID_ARGUMENT"
+    assert binding.status_string(UNS) == "FA_ERR_UNSUPPORTED"
+    assert binding.status_string(binding.FA_ERR_HIP) == "FA_ERR_HIP"
+    assert binding.status_string(99) == "FA_ERR_UNKNOWN"
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, N=16, d=64, dtype=1, causal=0, scale=0.125):
+    return L.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, dtype, causal, scale, None)
+
+
+def bwd(L, ws_bytes=1 << 20, B=1, Hq=2, Hkv=1, N=16, d=64, dtype=1, scale=0.125, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws")}
+    p.update(ptrs)
+    return L.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"], p["ws"],
+                    ws_bytes, B, Hq, Hkv, N, d, dtype, 0, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(o=None), INV), (dict(lse=None), INV),
+    (dict(q=P + 8), INV), (dict(lse=P + 4), INV),
+    (dict(B=-1), INV), (dict(N=-5), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV),
+    (dict(Hq=3, Hkv=2), INV), (dict(d=0), INV),
+    (dict(d=96), UNS), (dict(d=256), UNS), (dict(d=32), UNS), (dict(dtype=7), UNS),
+    (dict(scale=0.0), INV), (dict(scale=-0.125), INV), (dict(scale=math.nan), INV), (dict(scale=math.inf), INV),
+    (dict(N=1 << 40), INV), (dict(B=1 << 33), INV),
+])
+def test_fwd_rejects(L, kw, expect):
+    assert fwd(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(B=0, q=None, k=None, v=None, o=None, lse=None)])
+def test_fwd_empty_is_noop(L, kw):
+    assert fwd(L, **kw) == OK
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(do=None), INV), (dict(dq=None), INV), (dict(dk=None), INV), (dict(dv=None), INV), (dict(ws=None), INV),
+    (dict(ws=P + 2), INV), (dict(ws_bytes=0), INV), (dict(Hq=4, Hkv=3), INV), (dict(d=80), UNS),
+    (dict(scale=math.nan), INV),
+])
+def test_bwd_rejects(L, kw, expect):
+    assert bwd(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+def test_bwd_workspace_too_small(L):
+    need = L.fa_bwd_workspace_size(1, 2, 1, 16, 64, 1, 0)
+    assert need >= (2 * 16 + 2 * 16 * 64) * 4
+    assert bwd(L, ws_bytes=need - 1) == INV
+    assert "workspace" in binding.last_error()
+
+
+def test_workspace_size_values(L):
+    # D row terms [B,Hq,N] fp32 + dQ accumulator [B,Hq,N,d] fp32, each rounded up to 256 bytes
+    def rnd(x):
+        return (x + 255) // 256 * 256
+    for B, Hq, Hkv, N, d in ((1, 16, 16, 4096, 128), (2, 32, 8, 8192, 128), (1, 1, 1, 1, 64), (3, 6, 2, 1000, 64)):
+        got = L.fa_bwd_workspace_size(B, Hq, Hkv, N, d, 1, 1)
+        assert got == rnd(B * Hq * N * 4) + rnd(B * Hq * N * d * 4)
+    assert L.fa_bwd_workspace_size(1, 3, 2, 16, 64, 1, 0) == 0
+    assert L.fa_bwd_workspace_size(1, 2, 1, 16, 96, 1, 0) == 0
+
+
+def test_python_binding_validates_before_the_abi():
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q)          # CPU tensors are refused before any call
+    with pytest.raises(TypeError):
+        binding._dtype_code(torch.zeros(1, dtype=torch.float32))
