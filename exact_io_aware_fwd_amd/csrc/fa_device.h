@@ -61,6 +61,13 @@ template <> struct Elt<f16_tag> {
   }
 };
 
+static __device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
 // 8 contiguous bytes of LDS, read transposed across each 16-lane group.
 static __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -84,6 +91,22 @@ static __device__ __forceinline__ float half_sum(float x) {
 }
 
 static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Compiler fences on values (device pass only; the host pass never sees VGPR constraints).
+// opaque(x): x is redefined here, so nothing computed from it is hoisted above this point.
+// keep(x):   x must be computed before this point (no sinking into later blocks).
+template <class T>
+static __device__ __forceinline__ void opaque(T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+}
+template <class T>
+static __device__ __forceinline__ void keep(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
 
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;

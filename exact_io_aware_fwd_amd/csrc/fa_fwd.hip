@@ -6,24 +6,38 @@
 // output kept on chip, one division at the end; causal tiles above the diagonal
 // are skipped.  Work split as in the section "FlashAttention-2: better work
 // partitioning" (Figure 6): one workgroup per (batch, head, query block), so no
-// atomics and a bitwise-deterministic result.
+// atomics and a bitwise-deterministic result.  The rescaling threshold follows
+// the section "FlashAttention-4: Blackwell co-design" (conditional softmax
+// rescaling); the overlap of score products with the softmax of the previous
+// tile follows the section "FlashAttention-3" (matmul/softmax interleaving),
+// realised here inside each wave's instruction stream.
 //
 // gfx950 design.
-//  * A workgroup owns BR = 32*NW query rows; wave w owns rows [32w, 32w+32).
+//  * A workgroup owns 256 query rows, 8 waves x 32 rows; one workgroup per CU,
+//    two waves per SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: every
-//    lane then holds the scores of ONE query (lane % 32) for 32 keys, so the row
-//    max and row sum are in-lane plus one permlane32 swap, and the probabilities
-//    are already in the B-operand layout of O^T += V^T P^T (no LDS round trip).
-//    The key order inside each 16-key MFMA step is permuted consistently on both
+//    lane holds the scores of ONE query (lane % 32) for 32 keys, so the row max
+//    and row sum are in-lane plus one permlane32 swap, and the probabilities are
+//    already in the B-operand layout of O^T += V^T P^T (no LDS round trip).  The
+//    key order inside each 16-key MFMA step is permuted consistently on both
 //    operands, which the sum over keys does not see.
-//  * Q stays in VGPRs for the whole key loop; K and V tiles (BC = 64 keys) are
-//    double-buffered in LDS, prefetched from HBM into VGPRs one tile ahead.
-//  * V stays row-major in LDS; ds_read_b64_tr_b16 delivers it transposed as the
-//    A operand.
-//  * Scores are kept in log2 units: p = exp2(s * scale*log2e - m * scale*log2e).
-//  * Causal: a workgroup stops at the last tile its rows can see; inside the
-//    diagonal band a wave skips tiles entirely above its rows and masks only
-//    tiles that cross its diagonal (or the sequence end).
+//  * Q stays in VGPRs for the whole key loop.  K and V tiles of 64 keys go from
+//    HBM straight into LDS (global_load_lds, 16 bytes per lane, three slots, two
+//    tiles in flight).  Rows are padded to a pitch of row+16 bytes for K and
+//    row+64 bytes for V: with the 64 four-byte banks of the CDNA4 LDS, 16 lanes
+//    reading 16 bytes from 16 consecutive K rows, and 32 lanes reading 8 bytes
+//    from 4 consecutive V rows (ds_read_b64_tr_b16), then hit distinct banks
+//    (measured free of bank conflicts), and every LDS address is a lane
+//    constant plus an immediate.  The loads use buffer descriptors that end at
+//    row N, so rows past the sequence end land as zeros.
+//  * Software pipeline per wave: the products S_{j+1} = K_{j+1} Q^T are issued
+//    while the softmax of tile j runs, then O^T += V_j^T P_j.
+//  * Scores are kept in log2 units.  The reference max is raised only when a
+//    row's max exceeds it by more than 8 (so P <= 256), and O is rescaled only
+//    when some lane of the wave raised it.
+//  * Causal: a workgroup stops at the last tile its rows can see; each wave stops
+//    computing after the tile holding its diagonal, the only tile it masks
+//    (besides the sequence tail).
 //  * Block ids are remapped so that all query blocks sharing a K/V head run on
 //    one XCD (block ids are dealt round-robin over the 8 XCDs) and the longest
 //    causal blocks start first.
@@ -31,6 +45,34 @@
 #include "fa_internal.h"
 
 namespace fa {
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Tile t of K and V (BC = 64 rows each) from HBM into LDS slot t % 3 with wave-wide
+// 16-byte-per-lane loads through buffer descriptors that end at row N (rows past the
+// end arrive as zeros).  Load n = wave + NW*i fills bytes [1024n, 1024n+1024) of the
+// slot (K tile first, then V tile); this lane's bytes come from byte doff[i] of the
+// tile's rows.
+template <int ROWB, int KI, int NI, int IPW, int NW, int SLOT>
+__device__ __forceinline__ void dma_tile(const unsigned char* Kg, const unsigned char* Vg, int N, int t,
+                                         int wave, const int* doff, unsigned char* lds) {
+  const int kb = t * 64;
+  const int bytes = (N - kb) * ROWB;
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kb * ROWB), (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (size_t)kb * ROWB), (short)0, bytes, 0x00020000);
+  unsigned char* base = lds + (t % 3) * SLOT;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int n = wave + NW * i;
+    if (n < KI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid*)(base + n * 1024), 16, doff[i], 0, 0, 0);
+    else if (n < NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid*)(base + n * 1024), 16, doff[i], 0, 0, 0);
+  }
+}
 
 // Block id -> (batch, query head, query block).  Blocks are dealt round-robin to
 // the 8 XCDs; when the number of (batch, kv-head) groups is a multiple of 8,
@@ -61,26 +103,30 @@ __device__ __forceinline__ void map_fwd_block(int nqb, int B, int Hq, int Hkv, i
   hq = (grp - b * Hkv) * G + gq;
 }
 
-template <class Tag, int D, int NW, bool CAUSAL>
-__global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
+template <class Tag, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
-  constexpr int BR = 32 * NW;          // query rows per workgroup
-  constexpr int BC = 64;               // keys per tile
-  constexpr int NT = NW * 64;          // threads
-  constexpr int ROWB = D * 2;          // bytes of one K/V/Q/O row
-  constexpr int PK = ROWB + 16;        // LDS pitch of K rows (row-contiguous 16-byte reads)
-  constexpr int PV = ROWB + 32;        // LDS pitch of V rows (transposing 8-byte reads)
-  constexpr int KT = BC * PK;
-  constexpr int STAGE = KT + BC * PV;
-  constexpr int CH_ROW = D / 8;        // 16-byte chunks per row
-  constexpr int CH_T = BC * CH_ROW;    // chunks per K (or V) tile
-  constexpr int CPT = 2 * CH_T / NT;   // chunks each thread moves per tile
-  static_assert(CPT * NT == 2 * CH_T && CH_T % NT == 0, "tile load split");
+  constexpr int NW = 8;                 // waves per workgroup
+  constexpr int BR = 32 * NW;           // query rows per workgroup
+  constexpr int BC = 64;                // keys per tile
+  constexpr int ROWB = D * 2;           // bytes of one row
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int PK = ROWB + 16;         // LDS pitch of K rows
+  constexpr int PV = ROWB + 64;         // LDS pitch of V rows
+  constexpr int KBYTES = BC * PK, VBYTES = BC * PV;
+  constexpr int SLOT = KBYTES + VBYTES; // one K tile then one V tile
+  constexpr int KI = KBYTES / 1024;     // wave-wide 16-byte-per-lane loads per K tile
+  constexpr int NI = KI + VBYTES / 1024;
+  constexpr int IPW = (NI + NW - 1) / NW;
+  constexpr int NE = D / 32;            // 32-row blocks of O^T
+  constexpr int NS = D / 16;            // k-steps of S^T
+  constexpr float TAU = 8.f;            // rescale threshold (log2 units)
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles are whole wave loads");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
 
@@ -98,146 +144,252 @@ __global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
   const int myq = qw + r32;        // the query this lane's scores belong to
 
   // Q^T as the B operand: lane holds Q[myq][16s + 8hh .. +7]
-  u32x4 qf[D / 16];
+  u32x4 qf[NS];
   if (myq < N) {
     const unsigned char* qp = Qg + (size_t)myq * ROWB + 16 * hh;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = *(const u32x4*)(qp + 32 * s);
+    for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qp + 32 * s);
   } else {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) qf[s] = u32x4{0, 0, 0, 0};
   }
 
   const int nkv = (N + BC - 1) / BC;
-  int ntile = nkv;
-  if (CAUSAL) ntile = min(nkv, (min(q0 + BR, N) - 1) / BC + 1);
+  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
 
-  u32x4 stage[CPT];
-  auto gload = [&](int j) {
-    const int kbase = j * BC;
-    const bool full = kbase + BC <= N;
+  // ---- HBM -> LDS.  Load n of a tile (n = wave + NW*i) fills bytes [1024n, 1024n+1024)
+  // of the slot; this lane's 16 bytes come from byte doff[i] of the tile's rows.  Lanes
+  // landing on row padding re-fetch byte 0 (any valid address will do).  The loads go
+  // through a buffer descriptor whose range ends at row N, so rows past the end of the
+  // sequence arrive as zeros.
+  int doff[IPW];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * NT;
-      const int tens = (c * NT) / CH_T;  // compile-time: 0 = K, 1 = V
-      const int w = ci - tens * CH_T;
-      const int row = w / CH_ROW, col = w - (w / CH_ROW) * CH_ROW;
-      const unsigned char* src = (tens == 0 ? Kg : Vg) + (size_t)(kbase + row) * ROWB + col * 16;
-      if (full || kbase + row < N)
-        stage[c] = *(const u32x4*)src;
-      else
-        stage[c] = u32x4{0, 0, 0, 0};   // rows past the end: zero, so 0 * V stays finite
-    }
+  for (int i = 0; i < IPW; ++i) {
+    const int n = wave + NW * i;
+    const int P = n < KI ? PK : PV;
+    const int o = (n < KI ? n : n - KI) * 1024 + lane * 16;
+    const int row = o / P, col = o - (o / P) * P;
+    doff[i] = col < ROWB ? row * ROWB + col : 0;
+  }
+  auto dma = [&](int t) {
+    dma_tile<ROWB, KI, NI, IPW, NW, SLOT>(Kg, Vg, N, t, wave, doff, lds);
   };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = tid + c * NT;
-      const int tens = (c * NT) / CH_T;
-      const int w = ci - tens * CH_T;
-      const int row = w / CH_ROW, col = w - (w / CH_ROW) * CH_ROW;
-      unsigned char* dst = smem + buf * STAGE + (tens == 0 ? row * PK : KT + row * PV) + col * 16;
-      *(u32x4*)dst = stage[c];
-    }
-  };
+
+  // ---- per-lane LDS offsets (plus immediates) ----
+  // K (A operand of S^T): row 32c + r32, chunk 2st + hh
+  const int ka = r32 * PK + 16 * hh;
+  // V (A operand of O^T, read transposed): row 16t + 8u + R, element 32e + 16x + 4y
+  const int va = KBYTES + (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   const float c2 = a.scale_log2;
-  float m_run = -INFINITY;   // running max of the raw scores of query myq
-  float l_run = 0.f;         // running sum over this lane's half of the keys
-  f32x16 o[D / 32];
+  float mr = -INFINITY;       // reference max of query myq (log2 units)
+  float l_run = 0.f;          // running sum over this lane's half of the keys
+  f32x16 o[NE];
 #pragma unroll
-  for (int e = 0; e < D / 32; ++e)
+  for (int e = 0; e < NE; ++e)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[e][v] = 0.f;
 
-  // per-lane LDS offsets
-  const int koff = r32 * PK + 16 * hh;
-  const int voff = (4 * hh + ((lane & 15) >> 2)) * PV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // The pipeline works on 32-key units: unit u is half (u & 1) of tile u >> 1.
+  // LDS byte offsets of unit u's K rows / V rows for this lane, kept opaque so that
+  // every read below is "one register + immediate".
+  auto kbase = [&](int u) {
+    int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PK + ka;
+    opaque(r);
+    return r;
+  };
+  auto vbase = [&](int u) {
+    int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PV + va;
+    opaque(r);
+    return r;
+  };
+  auto kread = [&](int kb, int st) { return *(const u32x4*)(lds + kb + 32 * st); };
+  auto vread = [&](int vb, int h, int e) {
+    return cat(lds_read_tr(lds + vb + 16 * h * PV + 64 * e), lds_read_tr(lds + vb + (16 * h + 8) * PV + 64 * e));
+  };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
+  // Softmax pieces on the scores s of one unit (in log2 units after * c2).
+  auto rowmax = [&](const f32x16& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    return mx;
+  };
+  // new reference from the unit's row max; returns alpha = exp2(old - new), sets mref
+  auto newref = [&](float mx, bool& raise, float& mref) {
+    mx *= c2;
+    raise = mx > mr + TAU;
+    const float mnew = raise ? mx : mr;
+    const float alpha = (mr == -INFINITY) ? 0.f : fast_exp2(mr - mnew);
+    mref = (mnew == -INFINITY) ? 0.f : mnew;
+    mr = mnew;
+    return alpha;
+  };
+  auto packp = [&](const f32x16& s, int h) {
+    return u32x4{E::pack(s[8 * h + 0], s[8 * h + 1]), E::pack(s[8 * h + 2], s[8 * h + 3]),
+                 E::pack(s[8 * h + 4], s[8 * h + 5]), E::pack(s[8 * h + 6], s[8 * h + 7])};
+  };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
+  };
 
-  for (int j = 0; j < ntile; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntile) gload(j + 1);
-    const unsigned char* Ks = smem + buf * STAGE;
-    const unsigned char* Vs = Ks + KT;
-    const int k0 = j * BC;
-    if (!CAUSAL || k0 <= qw + 31) {
-      // S^T = K Q^T, two 32-key halves
-      f32x16 s[2];
+  // last unit this wave computes: the one holding its diagonal (causal) or the last
+  // holding a key of the sequence
+  const int ulast = (CAUSAL ? min(qw + 31, N - 1) : N - 1) / 32;
+
+  // K fragments of the next unit's first two k-steps, read ahead
+  u32x4 kpre0, kpre1;
+
+  // Unit u (u < ulast), hand-scheduled.  S-phase: NS slots, each one MFMA of S_{u+1}
+  // plus a share of the softmax of unit u; PV-phase: 2*NE slots, each one MFMA of
+  // O^T += V^T P plus two adds of the row sum.  LDS reads run two slots ahead.
+  auto step_main = [&](int u, f32x16& sc, f32x16& sn) {
+    const int kb = kbase(u + 1);
+    const int vb = vbase(u);
+    u32x4 kf[NS];
+    kf[0] = kpre0;
+    kf[1] = kpre1;
+    float mx0 = 0.f, mx = 0.f, alpha = 1.f, mref = 0.f;
+    bool raise = false;
+    u32x4 vf[2 * NE];
+    u32x4 pf[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+    for (int k = 0; k < NS; ++k) {
+      if (k == 0) sn = zero16();
+      sn = E::mma(kf[k], qf[k], sn);
+      if (k + 2 < NS) kf[k + 2] = kread(kb, k + 2);
+      if (k + 2 >= NS) vf[k + 2 - NS] = vread(vb, (k + 2 - NS) / NE, (k + 2 - NS) % NE);
+      if (k == 0) {
+        mx0 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[c][v] = 0.f;
-        const unsigned char* kp = Ks + 32 * c * PK + koff;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) s[c] = E::mma(*(const u32x4*)(kp + 32 * st), qf[st], s[c]);
+        for (int v = 4; v < 8; ++v) mx0 = fmaxf(mx0, sc[v]);
       }
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
-      if (need_mask) {
+      if (k == 1) {
+        mx = mx0;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int v = 8; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+        mx = half_max(mx);
+        alpha = newref(mx, raise, mref);
+      }
+      if (k >= 2 && k < NS - 1) {
+        // exps spread over slots 2 .. NS-2
+        constexpr int nslot = NS - 3 > 0 ? NS - 3 : 1;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = k0 + 32 * c + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (key >= N || (CAUSAL && key > myq)) s[c][v] = -INFINITY;
+        for (int v = 0; v < 16; ++v)
+          if (2 + (v * nslot) / 16 == k) {
+            sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
+            keep(sc[v]);   // stays in this slot (no sinking past the rescale branch)
           }
       }
-      float mx = s[0][0];
+      if (k == NS - 1) {
+        if (NS <= 3) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[c][v]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float mref = (m_new == -INFINITY) ? 0.f : m_new * c2;
-      const float alpha = fast_exp2(m_run * c2 - mref);
-      float rs = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(s[c][v], c2, -mref));
-          s[c][v] = p;
-          rs += p;
+          for (int v = 0; v < 16; ++v) sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
-      // P^T as the B operand: step t covers keys [16t, 16t+16)
-      u32x4 pf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = t >> 1, v0 = 8 * (t & 1);
-        pf[t] = u32x4{E::pack(s[c][v0 + 0], s[c][v0 + 1]), E::pack(s[c][v0 + 2], s[c][v0 + 3]),
-                      E::pack(s[c][v0 + 4], s[c][v0 + 5]), E::pack(s[c][v0 + 6], s[c][v0 + 7])};
+        pf[0] = packp(sc, 0);
+        pf[1] = packp(sc, 1);
+        keep(pf[0]);
+        keep(pf[1]);
       }
-      // O^T += V^T P^T
-      const unsigned char* vp = Vs + voff;
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u32x4 af = cat(lds_read_tr(vp + 16 * t * PV + 64 * e), lds_read_tr(vp + (16 * t + 8) * PV + 64 * e));
-          o[e] = E::mma(af, pf[t], o[e]);
-        }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (j + 1 < ntile) swrite(buf ^ 1);
-    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) rescale(alpha);
+    __builtin_amdgcn_sched_barrier(0);
+    float rs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2 * NE; ++k) {
+      const int h = k / NE, e = k % NE;
+      o[e] = E::mma(vf[k], pf[h], o[e]);
+      if (k + 2 < 2 * NE) vf[k + 2] = vread(vb, (k + 2) / NE, (k + 2) % NE);
+      if (k == 2 * NE - 2) kpre0 = kread(kbase(u + 2), 0);
+      if (k == 2 * NE - 1) kpre1 = kread(kbase(u + 2), 1);
+      rs += sc[2 * k % 16] + sc[(2 * k + 1) % 16];
+      if (k == 2 * NE - 1 && 4 * NE < 16) {
+#pragma unroll
+        for (int v = 4 * NE; v < 16; ++v) rs += sc[v];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = fmaf(l_run, alpha, rs);
+  };
+
+  // The wave's last unit: diagonal (causal) and/or sequence tail; no next unit.
+  auto step_last = [&](int u, f32x16& sc) {
+    const int k0 = u * 32;
+    int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
+    if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = -INFINITY;
+    bool raise;
+    float mref;
+    const float alpha = newref(half_max(rowmax(sc)), raise, mref);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) rescale(alpha);
+    const u32x4 pf[2] = {packp(sc, 0), packp(sc, 1)};
+    const int vb = vbase(u);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] = E::mma(vread(vb, h, e), pf[h], o[e]);
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rs += sc[v];
+    l_run = fmaf(l_run, alpha, rs);
+  };
+
+  auto step = [&](int u, f32x16& sc, f32x16& sn) {
+    if (u < ulast) step_main(u, sc, sn);
+    else if (u == ulast) step_last(u, sc);
+  };
+
+  // ---- pipeline: two tiles in flight in LDS; S of unit u+1 formed during softmax of u ----
+  dma(0);
+  if (ntile > 1) dma(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  f32x16 sa, sb;
+  {
+    const int kb = kbase(0);
+    sa = zero16();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) sa = E::mma(kread(kb, st), qf[st], sa);
+    kpre0 = kread(kbase(1), 0);
+    kpre1 = kread(kbase(1), 1);
+  }
+  // Tiles [0, J1): every wave has both units ahead of its last one (branch-free loop).
+  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;   // the smallest ulast
+  const int J1 = min(ntile, ulast0 / 2);
+  auto tile_start = [&](int j) {
+    if (j > 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile j+1 landed
+      __syncthreads();                                   // everyone's; slot (j-1)%3 is free
+    }
+    if (j + 2 < ntile) dma(j + 2);
+  };
+  for (int j = 0; j < J1; ++j) {
+    tile_start(j);
+    step_main(2 * j, sa, sb);
+    step_main(2 * j + 1, sb, sa);
+  }
+  for (int j = J1; j < ntile; ++j) {
+    tile_start(j);
+    step(2 * j, sa, sb);
+    step(2 * j + 1, sb, sa);
   }
 
-  // epilogue: O = O^T / l, LSE = ln(2) * (m*scale*log2e + log2 l)
+  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
   const float l_tot = half_sum(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
     unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * e + 8 * g + 4 * hh;
@@ -245,27 +397,23 @@ __global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
                          E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
         *(u32x2*)(Og + d0 * 2) = w;
       }
-    if (hh == 0) {
-      const float mref = m_run * c2;
-      a.lse[qhead + myq] = (mref + log2f(l_tot)) * kLn2;
-    }
+    if (hh == 0) a.lse[qhead + myq] = (mr + log2f(l_tot)) * kLn2;
   }
 }
 
-template <class Tag, int D, int NW, bool CAUSAL>
+template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BR = 32 * NW;
+  constexpr int BR = 256;
   const int nqb = (a.N + BR - 1) / BR;
   const long long nblocks = (long long)a.B * a.Hq * nqb;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<Tag, D, NW, CAUSAL>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream) {
-  constexpr int NW = 8;
-#define FA_FWD_CASE(TAG, D)                                                       \
-  return causal ? launch_fwd_t<TAG, D, NW, true>(a, stream) : launch_fwd_t<TAG, D, NW, false>(a, stream)
+#define FA_FWD_CASE(TAG, D) \
+  return causal ? launch_fwd_t<TAG, D, true>(a, stream) : launch_fwd_t<TAG, D, false>(a, stream)
   if (bf16) {
     if (d == 128) FA_FWD_CASE(bf16_tag, 128);
     FA_FWD_CASE(bf16_tag, 64);

@@ -33,6 +33,13 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n)
 
 
+def test_no_undefined_kernel_stubs():
+    """Every kernel launched by the library has its host-side stub compiled in."""
+    out = subprocess.run(["nm", "-D", binding.LIB_PATH], capture_output=True, text=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not undefined, undefined
+
+
 def test_status_strings(L):
     assert binding.status_string(OK) == "FA_OK"
     assert binding.status_string(INV) == "FA_ERR_INVALID_ARGUMENT"
