@@ -12,14 +12,26 @@ are under `passes`.  `cpu_baseline` times the fp64 oracle on a bounded sample
 of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--fwd-only]
+
+Profiling helpers (rocprofv3 runs of this same script):
+    python bench.py --copy-calibration          # a plain 1 GiB device copy, for HBM counters
+    python bench.py --summarize DIR [--pmc]     # rocprofv3 CSV -> markdown summary on stdout
+    python bench.py --record-traffic DIR ...    # FETCH/WRITE per dispatch -> profiles/traffic.json
+
+`roofline.traffic` is filled from profiles/traffic.json only while the kernel sources
+hash to the value recorded with the counters; otherwise it is null.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
 import time
+from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -35,7 +47,105 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward pass (profiling)")
     p.add_argument("--cpu-heads", type=int, default=12, help="query heads in the CPU-baseline sample")
+    p.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy and exit")
+    p.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 CSV output under DIR and exit")
+    p.add_argument("--pmc", action="store_true", help="with --summarize: counter CSVs instead of kernel trace")
+    p.add_argument("--record-traffic", nargs=3, metavar=("KERNEL_DIR", "COPY_DIR", "KERNEL_SUBSTR"),
+                   help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE runs and exit")
     return p.parse_args()
+
+
+KERNEL_SOURCES = {
+    "fwd": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h"],
+    "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h"],
+}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, five times (for counter scaling)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 5}))
+
+
+def _read_csv(pattern):
+    rows = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def pmc_per_dispatch(directory):
+    """{kernel name: {counter: mean value per dispatch}} from rocprofv3 --pmc CSV output."""
+    tot = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(set)
+    for r in _read_csv(os.path.join(directory, "**", "*counter_collection.csv")):
+        k = r["Kernel_Name"]
+        tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[(k, r["Counter_Name"])].add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[(k, c)]) for c, v in cs.items()} for k, cs in tot.items()}
+
+
+def summarize(directory, pmc):
+    if pmc:
+        for k, cs in pmc_per_dispatch(directory).items():
+            print(f"### `{k}`\n\n| counter | per dispatch |\n|---|---|")
+            for c, v in sorted(cs.items()):
+                print(f"| {c} | {v:.6g} |")
+            print()
+        return
+    rows = _read_csv(os.path.join(directory, "**", "*kernel_stats.csv"))
+    print("| kernel | calls | total ns | average ns | min ns | max ns | % |\n|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| `{r['Name']}` | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+              f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f} |")
+
+
+def record_traffic(kdir, cdir, substr):
+    # every kernel whose name contains substr runs once per call of the pass: sum them
+    kern = {k: v for k, v in pmc_per_dispatch(kdir).items() if substr in k}
+    copy = {k: v for k, v in pmc_per_dispatch(cdir).items() if "copy" in k.lower()}
+    if not kern or not copy:
+        raise SystemExit(f"expected kernels matching {substr!r} and a copy kernel; got {list(kern)}, {list(copy)}")
+    kname = " + ".join(sorted(kern))
+    kc = {c: sum(v.get(c, 0.0) for v in kern.values()) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    cc = max(copy.values(), key=lambda c: c.get("FETCH_SIZE", 0) + c.get("WRITE_SIZE", 0))
+    kib = COPY_BYTES / 1024
+    fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
+    write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
+    kind = "bwd" if "bwd" in substr else "fwd"
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
+                  "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
+                  "copy_fetch_factor": fetch_factor, "copy_write_factor": write_factor}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    json.dump(data, open(TRAFFIC_JSON, "w"), indent=1)
+    print(json.dumps(data[kind]))
+
+
+def traffic_bytes(kind: str):
+    """Per-launch HBM bytes from the recorded counters, if they match the current sources."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    rec = json.load(open(TRAFFIC_JSON)).get(kind)
+    if not rec or rec.get("source_hash") != source_hash(kind):
+        return None
+    if None in (rec.get("fetch_kib"), rec.get("write_kib"), rec.get("copy_fetch_factor"), rec.get("copy_write_factor")):
+        return None
+    return 1024.0 * (rec["fetch_kib"] * rec["copy_fetch_factor"] + rec["write_kib"] * rec["copy_write_factor"])
 
 
 def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
@@ -70,6 +180,15 @@ def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.pmc)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
@@ -131,10 +250,14 @@ def main():
         passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_main_kernel + bwd_dq_kernel", "launches": 3,
                          "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12}
         passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
+    def roofline(kind):
+        return {"bound": "mfma", "achieved": passes[kind]["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": passes[kind]["frac"], "traffic": traffic_bytes(kind), "kernel": passes[kind]["kernel"],
+                "per_launch_flops": f_fwd if kind == "fwd" else f_bwd, "avg_ms": passes[kind]["ms"],
+                "algorithmic_bytes": (metrics.fwd_bytes if kind == "fwd" else metrics.bwd_bytes)(
+                    w.B, w.Hq, w.Hkv, w.N, w.d, 2)}
     dom = max(passes, key=lambda n: passes[n]["ms"])
-    roof = {"bound": "mfma", "achieved": passes[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
-            "frac": passes[dom]["frac"], "traffic": None, "kernel": passes[dom]["kernel"],
-            "per_launch_flops": f_fwd if dom == "fwd" else f_bwd, "avg_ms": passes[dom]["ms"]}
+    roof = roofline(dom)
 
     dt_name = {torch.bfloat16: "bf16", torch.float16: "fp16"}[q.dtype]
     rec = {
@@ -147,6 +270,7 @@ def main():
                    "flops_per_step": f_fwd + f_bwd},
         "frac_of_peak": value / peak,
         "roofline": roof,
+        "roofline_fwd": roofline("fwd"),
         "passes": passes,
     }
     if not args.no_cpu_baseline:

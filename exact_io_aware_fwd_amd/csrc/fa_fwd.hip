@@ -43,65 +43,9 @@
 //    causal blocks start first.
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fa_tiles.h"
 
 namespace fa {
-
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-
-// Tile t of K and V (BC = 64 rows each) from HBM into LDS slot t % 3 with wave-wide
-// 16-byte-per-lane loads through buffer descriptors that end at row N (rows past the
-// end arrive as zeros).  Load n = wave + NW*i fills bytes [1024n, 1024n+1024) of the
-// slot (K tile first, then V tile); this lane's bytes come from byte doff[i] of the
-// tile's rows.
-template <int ROWB, int KI, int NI, int IPW, int NW, int SLOT>
-__device__ __forceinline__ void dma_tile(const unsigned char* Kg, const unsigned char* Vg, int N, int t,
-                                         int wave, const int* doff, unsigned char* lds) {
-  const int kb = t * 64;
-  const int bytes = (N - kb) * ROWB;
-  const __amdgpu_buffer_rsrc_t kr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (size_t)kb * ROWB), (short)0, bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (size_t)kb * ROWB), (short)0, bytes, 0x00020000);
-  unsigned char* base = lds + (t % 3) * SLOT;
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int n = wave + NW * i;
-    if (n < KI)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid*)(base + n * 1024), 16, doff[i], 0, 0, 0);
-    else if (n < NI)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid*)(base + n * 1024), 16, doff[i], 0, 0, 0);
-  }
-}
-
-// Block id -> (batch, query head, query block).  Blocks are dealt round-robin to
-// the 8 XCDs; when the number of (batch, kv-head) groups is a multiple of 8,
-// XCD x serves groups x, x+8, ... so their K/V stay in that XCD's L2.  Within an
-// XCD, slots run over query blocks from the last (longest when causal) down.
-__device__ __forceinline__ void map_fwd_block(int nqb, int B, int Hq, int Hkv, int& b, int& hq,
-                                              int& iq) {
-  const int G = Hq / Hkv;
-  const int ngroups = B * Hkv;
-  const int bid = blockIdx.x;
-  int grp, gq, iq_rev;
-  if ((ngroups & 7) == 0) {
-    const int x = bid & 7, s = bid >> 3;
-    const int per = (ngroups >> 3) * G;  // blocks per query-block index on one XCD
-    iq_rev = s / per;
-    const int rest = s - iq_rev * per;
-    grp = x + 8 * (rest / G);
-    gq = rest - (rest / G) * G;
-  } else {
-    const int per = ngroups * G;
-    iq_rev = bid / per;
-    const int rest = bid - iq_rev * per;
-    grp = rest / G;
-    gq = rest - grp * G;
-  }
-  iq = nqb - 1 - iq_rev;
-  b = grp / Hkv;
-  hq = (grp - b * Hkv) * G + gq;
-}
 
 template <class Tag, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
@@ -111,17 +55,15 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   constexpr int BC = 64;                // keys per tile
   constexpr int ROWB = D * 2;           // bytes of one row
   constexpr int CH = D / 8;             // 16-byte chunks per row
-  constexpr int PK = ROWB + 16;         // LDS pitch of K rows
-  constexpr int PV = ROWB + 64;         // LDS pitch of V rows
-  constexpr int KBYTES = BC * PK, VBYTES = BC * PV;
-  constexpr int SLOT = KBYTES + VBYTES; // one K tile then one V tile
-  constexpr int KI = KBYTES / 1024;     // wave-wide 16-byte-per-lane loads per K tile
-  constexpr int NI = KI + VBYTES / 1024;
-  constexpr int IPW = (NI + NW - 1) / NW;
+  constexpr int PK = ROWB + 16;         // LDS pitch of K rows (16-byte row reads)
+  constexpr int PV = ROWB + 64;         // LDS pitch of V rows (transposing reads)
+  using Tiles = TilePair<ROWB, PK, PV, NW>;
+  constexpr int KBYTES = Tiles::ABYTES;
+  constexpr int SLOT = Tiles::SLOT;
+  constexpr int IPW = Tiles::IPW;
   constexpr int NE = D / 32;            // 32-row blocks of O^T
   constexpr int NS = D / 16;            // k-steps of S^T
   constexpr float TAU = 8.f;            // rescale threshold (log2 units)
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles are whole wave loads");
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
 
@@ -131,7 +73,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   const int N = a.N;
 
   int b, hq, iq;
-  map_fwd_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
   const int hkv = hq / (a.Hq / a.Hkv);
   const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
   const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
@@ -157,23 +99,10 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   const int nkv = (N + BC - 1) / BC;
   const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
 
-  // ---- HBM -> LDS.  Load n of a tile (n = wave + NW*i) fills bytes [1024n, 1024n+1024)
-  // of the slot; this lane's 16 bytes come from byte doff[i] of the tile's rows.  Lanes
-  // landing on row padding re-fetch byte 0 (any valid address will do).  The loads go
-  // through a buffer descriptor whose range ends at row N, so rows past the end of the
-  // sequence arrive as zeros.
+  // ---- HBM -> LDS: tile t of K and V into slot t % 3 ----
   int doff[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int n = wave + NW * i;
-    const int P = n < KI ? PK : PV;
-    const int o = (n < KI ? n : n - KI) * 1024 + lane * 16;
-    const int row = o / P, col = o - (o / P) * P;
-    doff[i] = col < ROWB ? row * ROWB + col : 0;
-  }
-  auto dma = [&](int t) {
-    dma_tile<ROWB, KI, NI, IPW, NW, SLOT>(Kg, Vg, N, t, wave, doff, lds);
-  };
+  Tiles::offsets(wave, lane, doff);
+  auto dma = [&](int t) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
 
   // ---- per-lane LDS offsets (plus immediates) ----
   // K (A operand of S^T): row 32c + r32, chunk 2st + hh

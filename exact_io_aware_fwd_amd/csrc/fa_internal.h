@@ -29,7 +29,6 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsum;   // workspace: D_i = sum_k dO_ik O_ik, [B, Hq, N] fp32
-  float* dqacc;  // workspace: dQ accumulator (unscaled), [B, Hq, N, d] fp32
   int B, Hq, Hkv, N;
   float scale;
   float scale_log2;
@@ -39,12 +38,9 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 
-// Workspace layout of the backward pass (bytes, each part 256-byte aligned).
+// Workspace of the backward pass: the fp32 row terms D, rounded up to 256 bytes.
 inline size_t bwd_dsum_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)((B * Hq * N * 4 + 255) / 256 * 256);
-}
-inline size_t bwd_dqacc_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d) {
-  return (size_t)((B * Hq * N * d * 4 + 255) / 256 * 256);
 }
 
 }  // namespace fa

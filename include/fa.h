@@ -72,7 +72,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: the fp32 row terms
- * D_i = sum_k dO_ik O_ik ([B,Hq,N]) and the fp32 dQ accumulator ([B,Hq,N,d]).
+ * D_i = sum_k dO_ik O_ik ([B,Hq,N]), rounded up to 256 bytes.
  * Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
@@ -85,9 +85,10 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
  * storage", Figure 5): P is recomputed block by block from the saved LSE.  The
  * gradient is the full softmax-attention gradient, dS = P * (dP - D) with
  * D_i = sum_k dO_ik O_ik, and dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO
- * (dK, dV summed over the query heads sharing a K/V head).  dQ is accumulated
- * with float32 atomic adds, so it is not bitwise reproducible run to run (the
- * Primer's same section discusses this property of the default backward).
+ * (dK, dV summed over the query heads sharing a K/V head).  dQ and dK/dV come
+ * from two passes that each own their output, with no atomic adds, so the
+ * result is bitwise reproducible run to run (the deterministic option discussed
+ * in the Primer's same section).
  *
  *   q, k, v, o, lse, dout : as produced for / by fa_fwd with the same arguments
  *   dq [B,Hq,N,d], dk/dv [B,Hkv,N,d]   outputs, `dtype`

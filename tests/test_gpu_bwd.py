@@ -91,6 +91,15 @@ def test_constant_v_gives_zero_dq_dk():
     assert rel_l2(dv.cpu(), dV) <= GRAD_TOL
 
 
+def test_backward_is_bitwise_deterministic():
+    q, k, v, do = (t.to("cuda:0") for t in workloads.random_case(21, 2, 8, 2, 1500, 128, torch.bfloat16, with_do=True))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    g2 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
+
+
 def test_empty_backward():
     q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda:0")
     lse = torch.empty(1, 2, 0, dtype=torch.float32, device="cuda:0")
