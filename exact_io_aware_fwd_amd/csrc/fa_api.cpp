@@ -116,7 +116,7 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
   (void)causal;
   bool empty = false;
   if (check_sizes(B, Hq, Hkv, N, d, dtype, &empty) != FA_OK) return 0;
-  return fa::bwd_dsum_bytes(B, Hq, N);
+  return fa::bwd_rowterm_bytes(B, Hq, N);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -135,7 +135,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
       (st = check_ptr(dq, "dq")) != FA_OK || (st = check_ptr(dk, "dk")) != FA_OK ||
       (st = check_ptr(dv, "dv")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
     return st;
-  const size_t need = fa::bwd_dsum_bytes(B, Hq, N);
+  const size_t need = fa::bwd_rowterm_bytes(B, Hq, N);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -150,7 +150,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dsum = static_cast<float*>(workspace);
+  a.rowterm = static_cast<float*>(workspace);
   a.B = (int)B;
   a.Hq = (int)Hq;
   a.Hkv = (int)Hkv;

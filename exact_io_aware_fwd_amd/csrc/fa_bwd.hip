@@ -14,23 +14,26 @@
 // output, as the same section's deterministic option does: it recomputes S and dP
 // once more, needs no atomics and no fp32 dQ buffer, and is bitwise reproducible.
 //
-//  1. row terms: D_i = sum_k dO_ik O_ik in fp32;
+//  1. row terms: LSE_i * log2(e) and D_i = sum_k dO_ik O_ik in fp32, as pairs;
 //  2. dQ pass: one workgroup per (batch, head, 32*NW-query block), the forward's
 //     structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K, V tiles
 //     streamed through LDS; P = exp2(S*scale*log2e - LSE*log2e),
 //     dS = P * (dP - D) in registers, dQ^T += K^T dS^T (K read transposed);
 //  3. dK/dV pass: one workgroup per (batch, K/V head, 128-key block); each of the
-//     4 waves owns 32 keys and keeps dK^T, dV^T for them in registers across all
-//     query heads of the group and all query blocks (from the diagonal when
-//     causal).  Per 32-query step: S = Q K^T, dP = dO V^T (lane = key),
-//     dV^T += dO^T P, dK^T += Q^T dS (Q^T, dO^T read transposed from LDS).
+//     4 waves owns 32 keys, holds their K and V in VGPRs and dK^T, dV^T in
+//     accumulators across all query heads of the group and all query blocks (from
+//     the diagonal when causal).  Q, dO and the row terms of each 32-query step go
+//     HBM -> LDS directly (three slots, two steps in flight).  Per step:
+//     S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P, dK^T += Q^T dS (Q^T,
+//     dO^T read transposed from LDS); the products of step n+1 are interleaved
+//     with the elementwise work of step n.
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
 namespace fa {
 
-// ---- 1. D_i = sum_k dO_ik O_ik --------------------------------------------------------
+// ---- 1. row terms: (LSE_i * log2 e, D_i = sum_k dO_ik O_ik) per query row ------------
 template <class Tag, int D>
 __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long long rows) {
   using E = Elt<Tag>;
@@ -50,63 +53,108 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && part == 0) a.dsum[row] = acc;
+  if (row < rows && part == 0) {
+    a.rowterm[2 * row] = a.lse[row] * kLog2e;
+    a.rowterm[2 * row + 1] = acc;
+  }
 }
 
 // ---- 3. dK, dV per key block ---------------------------------------------------------
+// XOR on the 16-byte chunk index of row r of a Q/dO tile in LDS.  The tiles are read
+// both by rows (16 bytes per lane, 16 consecutive rows) and transposed
+// (ds_read_b64_tr_b16, 8 bytes per lane from 4 consecutive rows); with this XOR
+// both patterns hit distinct banks (measured free of bank conflicts), and each
+// address is a lane constant XOR an instruction constant.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+
+// Q rows, dO rows (TB bytes each, 16-byte chunks XOR-swizzled by soff) and the
+// (LSE*log2e, D) row pairs of one query block into an LDS slot, straight from HBM.
+// `rows` rows remain from the block's first row on; rows past them arrive as zeros.
+// (A free function: the host pass of the compiler mishandles these builtins inside a
+// capturing lambda.)
+template <int ROWB, int TI, int LI, int NW, int TB>
+__device__ __forceinline__ void dkdv_load_step(const BwdArgs& a, size_t qrow, int rows, int wave, int lane,
+                                               const int* soff, unsigned char* slot) {
+  const int bytes = rows * ROWB;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.q + qrow * ROWB), (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const unsigned char*)a.dout + qrow * ROWB), (short)0, bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < LI; ++i) {
+    const int nn = wave + NW * i;
+    if (nn < TI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lvoid*)(slot + nn * 1024), 16, soff[i], 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lvoid*)(slot + nn * 1024), 16, soff[i], 0, 0, 0);
+  }
+  if (wave == 0) {
+    const __amdgpu_buffer_rsrc_t rr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.rowterm + 2 * qrow), (short)0, rows * 8, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lvoid*)(slot + 2 * TB), 4, lane * 4, 0, 0, 0);
+  }
+}
+
 template <class Tag, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
-  constexpr int NW = 4, NT = 256;
-  constexpr int BKV = 32 * NW;     // keys per workgroup
-  constexpr int BQ = 32;           // queries per step
+  constexpr int NW = 4;
+  constexpr int BKV = 32 * NW;        // keys per workgroup; wave w owns keys 32w .. 32w+31
+  constexpr int BQ = 32;              // queries per step
   constexpr int ROWB = D * 2;
-  constexpr int PK = ROWB + 16;    // K, V rows in LDS
-  constexpr int PQ = ROWB + 32;    // Q, dO rows in LDS (also read transposed)
-  constexpr int KV_BYTES = BKV * PK;
-  constexpr int QT_BYTES = BQ * PQ;
-  constexpr int CH_ROW = D / 8;
-  constexpr int QCH = BQ * CH_ROW;       // 16-byte chunks per Q (or dO) tile
-  constexpr int QCPT = 2 * QCH / NT;     // per thread per step
-  static_assert(QCPT * NT == 2 * QCH && QCH % NT == 0, "step load split");
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int NS = D / 16;          // k-steps of S and dP
+  constexpr int NE = D / 32;          // 32-row blocks of dK^T, dV^T
+  constexpr int TB = BQ * ROWB;       // bytes of one Q (or dO) tile
+  constexpr int TI = TB / 1024;       // wave-wide 16-byte-per-lane loads per tile
+  constexpr int RPI = 1024 / ROWB;    // rows per such load
+  constexpr int LI = (2 * TI + NW - 1) / NW;
+  constexpr int SLOT = 2 * TB + BQ * 8;   // Q tile, dO tile, (LSE*log2e, D) pairs
+  static_assert(2 * TI % NW == 0, "tile loads split evenly");
 
-  __shared__ __attribute__((aligned(16))) unsigned char Ks[KV_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char Vs[KV_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char Qs[2][QT_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char dOs[2][QT_BYTES];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dsums[2][BQ];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
   const int G = a.Hq / a.Hkv;
-  const int nkb = (N + BKV - 1) / BKV;
-  const int ngroups = a.B * a.Hkv;
-  const int jb = blockIdx.x / ngroups;          // key blocks nearest the start first (most work)
-  const int grp = blockIdx.x - jb * ngroups;
-  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
-  (void)nkb;
 
+  // block -> (key block, batch, kv head): groups x, x+8, ... on XCD x (their Q/dO stay in
+  // one L2), key blocks nearest the start (the most causal work) first
+  const int ngroups = a.B * a.Hkv;
+  int jb, grp;
+  if ((ngroups & 7) == 0) {
+    const int x = blockIdx.x & 7, sidx = blockIdx.x >> 3, per = ngroups >> 3;
+    jb = sidx / per;
+    grp = x + 8 * (sidx - jb * per);
+  } else {
+    jb = blockIdx.x / ngroups;
+    grp = blockIdx.x - jb * ngroups;
+  }
+  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
   const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
   const int k0 = jb * BKV;
-  const int kw = k0 + 32 * wave;     // first key of this wave
-  const int mykey = kw + r32;        // the key this lane's scores belong to
+  const int kw = k0 + 32 * wave;      // first key of this wave
+  const int mykey = kw + r32;         // the key this lane's scores belong to
 
-  // K and V tiles for the whole workgroup (rows past the end are zero)
-  {
-    const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
-    const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
-    for (int ci = tid; ci < BKV * CH_ROW; ci += NT) {
-      const int row = ci / CH_ROW, col = ci - (ci / CH_ROW) * CH_ROW;
-      u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
-      if (k0 + row < N) {
-        kx = *(const u32x4*)(Kg + (size_t)(k0 + row) * ROWB + col * 16);
-        vx = *(const u32x4*)(Vg + (size_t)(k0 + row) * ROWB + col * 16);
-      }
-      *(u32x4*)(Ks + row * PK + col * 16) = kx;
-      *(u32x4*)(Vs + row * PK + col * 16) = vx;
+  // K^T and V^T as B operands: lane holds row mykey, elements 16s + 8hh .. +7
+  u32x4 kf[NS], vf[NS];
+  if (mykey < N) {
+    const unsigned char* kp = (const unsigned char*)a.k + (kvhead + mykey) * ROWB + 16 * hh;
+    const unsigned char* vp = (const unsigned char*)a.v + (kvhead + mykey) * ROWB + 16 * hh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = *(const u32x4*)(kp + 32 * s);
+      vf[s] = *(const u32x4*)(vp + 32 * s);
     }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = vf[s] = u32x4{0, 0, 0, 0};
   }
 
   const int iq0 = CAUSAL ? k0 / BQ : 0;
@@ -114,141 +162,181 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const int per_head = nqb - iq0;
   const int nsteps = G * per_head;
 
-  u32x4 stage[QCPT];
-  float stage_l = 0.f;
-  auto gload = [&](int step) {
-    const int g = step / per_head;
-    const int qb = (iq0 + (step - g * per_head)) * BQ;
-    const size_t qhead = (size_t)(b * a.Hq + hkv * G + g) * (size_t)N;
-    const bool full = qb + BQ <= N;
+  // ---- HBM -> LDS: step n (query head hkv*G + n / per_head, query block
+  // iq0 + n % per_head) into slot n % 3.  Tile load nn = wave + NW*i covers slot bytes
+  // [1024nn, 1024nn+1024) (Q tile, then dO tile); lane's 16 bytes come from byte soff[i]
+  // of the tile's rows (chunks XOR-swizzled).  Rows past N arrive as zeros.
+  int soff[LI];
 #pragma unroll
-    for (int c = 0; c < QCPT; ++c) {
-      const int ci = tid + c * NT;
-      const int tens = (c * NT) / QCH;   // 0 = Q, 1 = dO
-      const int w = ci - tens * QCH;
-      const int row = w / CH_ROW, col = w - (w / CH_ROW) * CH_ROW;
-      const unsigned char* src = (const unsigned char*)(tens == 0 ? a.q : a.dout) +
-                                 ((qhead + qb + row) * ROWB) + col * 16;
-      stage[c] = (full || qb + row < N) ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-    }
-    if (tid < 2 * BQ) {
-      const int r = tid & (BQ - 1);
-      if (qb + r < N)
-        stage_l = (tid < BQ) ? a.lse[qhead + qb + r] * kLog2e : a.dsum[qhead + qb + r];
-      else
-        stage_l = 0.f;
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < QCPT; ++c) {
-      const int ci = tid + c * NT;
-      const int tens = (c * NT) / QCH;
-      const int w = ci - tens * QCH;
-      const int row = w / CH_ROW, col = w - (w / CH_ROW) * CH_ROW;
-      unsigned char* dst = (tens == 0 ? Qs[buf] : dOs[buf]) + row * PQ + col * 16;
-      *(u32x4*)dst = stage[c];
-    }
-    if (tid < 2 * BQ) {
-      if (tid < BQ) lse2s[buf][tid] = stage_l;
-      else dsums[buf][tid - BQ] = stage_l;
-    }
-  };
-
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      dk[e][v] = 0.f;
-      dv[e][v] = 0.f;
-    }
-
-  const float c2 = a.scale_log2;
-  const int rowoff = r32 * PQ + 16 * hh;                       // Q/dO row reads
-  const int keyoff = (32 * wave + r32) * PK + 16 * hh;         // K/V row reads
-  const int troff = (4 * hh + ((lane & 15) >> 2)) * PQ + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-
-  if (nsteps > 0) {
-    gload(0);
-    swrite(0);
+  for (int i = 0; i < LI; ++i) {
+    const int nn = wave + NW * i;
+    const int row = (nn % TI) * RPI + lane / CH;
+    soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
   }
-  __syncthreads();
+  auto dma = [&](int n) __attribute__((always_inline)) {
+    const int g = n / per_head;
+    const int qb = (iq0 + n - g * per_head) * BQ;
+    const size_t qrow = (size_t)(b * a.Hq + hkv * G + g) * (size_t)N + qb;
+    dkdv_load_step<ROWB, TI, LI, NW, TB>(a, qrow, N - qb, wave, lane, soff, lds + (n % 3) * SLOT);
+  };
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const int g = step / per_head;
-    const int qb = (iq0 + (step - g * per_head)) * BQ;
-    if (step + 1 < nsteps) gload(step + 1);
+  // ---- per-lane LDS addresses ----
+  // rows (A of S = Q K^T and dP = dO V^T): row r32, chunk 2st + hh
+  int rowa[NS];
+  {
+    const int a0 = r32 * ROWB + ((hh ^ swz<CH>(r32)) << 4);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) rowa[st] = a0 ^ (st << 5);
+  }
+  // transposed (A of dV^T = dO^T P and dK^T = Q^T dS): rows 16t + 8u + R, elements 32e + 16x + 4y
+  int tra[2 * NE];
+  {
+    const int R = 4 * hh + ((lane & 15) >> 2), x = (lane >> 4) & 1, y = lane & 3;
+    int lp;
+    if constexpr (CH == 16) lp = (2 * x) ^ (y >> 1) ^ ((R & 3) << 2) ^ hh;
+    else lp = (2 * x) ^ (y >> 1) ^ (((R >> 1) & 3) << 1);
+    const int al = R * ROWB + (lp << 4) + 8 * (y & 1);
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) tra[2 * e + u] = al ^ ((CH == 16 ? ((4 * e) ^ (2 * u)) : ((4 * e) ^ u)) << 4);
+  }
+  auto slotp = [&](int n) __attribute__((always_inline)) {
+    int r = (n % 3) * SLOT;
+    opaque(r);
+    return r;
+  };
+  auto rowrd = [&](int base, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + base + rowa[st]); };
+  auto trrd = [&](int base, int t, int e) __attribute__((always_inline)) {
+    return cat(lds_read_tr(lds + base + 16 * t * ROWB + tra[2 * e]),
+               lds_read_tr(lds + base + (16 * t + 8) * ROWB + tra[2 * e + 1]));
+  };
 
-    const unsigned char* Qb = Qs[buf];
-    const unsigned char* dOb = dOs[buf];
-    // S = Q K^T and dP = dO V^T for (32 queries) x (this wave's 32 keys)
-    f32x16 s, dp;
+  f32x16 dk[NE], dv[NE];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s[v] = 0.f;
-      dp[v] = 0.f;
-    }
+  for (int e = 0; e < NE; ++e) {
+    dk[e] = zero16();
+    dv[e] = zero16();
+  }
+  const float c2 = a.scale_log2;
+
+  // step n's query block and head
+  auto qblock = [&](int n) __attribute__((always_inline)) {
+    const int g = n / per_head;
+    return (iq0 + n - g * per_head) * BQ;
+  };
+  // wave activity and masking for step n (all wave-uniform)
+  auto active = [&](int n) __attribute__((always_inline)) { return n < nsteps && (!CAUSAL || kw <= qblock(n)); };
+  auto masked = [&](int n) __attribute__((always_inline)) {
+    const int qb = qblock(n);
+    return (CAUSAL && kw == qb) || qb + BQ > N || kw + 32 > N;
+  };
+
+  // S = Q K^T and dP = dO V^T of step n
+  auto products = [&](int n, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    const int base = slotp(n);
+    s = zero16();
+    dp = zero16();
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      s = E::mma(*(const u32x4*)(Qb + rowoff + 32 * st), *(const u32x4*)(Ks + keyoff + 32 * st), s);
-      dp = E::mma(*(const u32x4*)(dOb + rowoff + 32 * st), *(const u32x4*)(Vs + keyoff + 32 * st), dp);
+    for (int st = 0; st < NS; ++st) {
+      s = E::mma(rowrd(base, st), kf[st], s);
+      dp = E::mma(rowrd(base + TB, st), vf[st], dp);
     }
-    // P and dS; lane holds key `mykey`, rows q = 8*(v/4) + 4*hh + v%4
-    float lse2[16], dsv[16];
+  };
+  // P and dS of step n in place (s -> p, dp -> ds) for elements [lo, hi); rows q = 8(v/4) + 4hh + v%4
+  auto elementwise = [&](int base, f32x16& s, f32x16& dp, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const f32x4 l4 = *(const f32x4*)&lse2s[buf][8 * a4 + 4 * hh];
-      const f32x4 d4 = *(const f32x4*)&dsums[buf][8 * a4 + 4 * hh];
+      if (4 * a4 + 3 < lo || 4 * a4 >= hi) continue;
+      const f32x4 t0 = *(const f32x4*)(lds + base + 2 * TB + (8 * a4 + 4 * hh) * 8);
+      const f32x4 t1 = *(const f32x4*)(lds + base + 2 * TB + (8 * a4 + 4 * hh) * 8 + 16);
+      const float l2[4] = {t0[0], t0[2], t1[0], t1[2]}, dd[4] = {t0[1], t0[3], t1[1], t1[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lse2[4 * a4 + i] = l4[i];
-        dsv[4 * a4 + i] = d4[i];
+      for (int bb = 0; bb < 4; ++bb) {
+        const int v = 4 * a4 + bb;
+        if (v < lo || v >= hi) continue;
+        const float p = fast_exp2(fmaf(s[v], c2, -l2[bb]));
+        s[v] = p;
+        dp[v] = p * (dp[v] - dd[bb]);
+        keep(s[v]);
+        keep(dp[v]);
       }
     }
-    const bool need_mask = (qb + BQ > N) || (k0 + BKV > N) || (CAUSAL && kw + 31 > qb);
+  };
+  auto pack = [&](const f32x16& s, int t) __attribute__((always_inline)) {
+    return u32x4{E::pack(s[8 * t + 0], s[8 * t + 1]), E::pack(s[8 * t + 2], s[8 * t + 3]),
+                 E::pack(s[8 * t + 4], s[8 * t + 5]), E::pack(s[8 * t + 6], s[8 * t + 7])};
+  };
+  // dV^T += dO^T P, dK^T += Q^T dS for step n
+  auto accumulate = [&](int base, const u32x4* pf, const u32x4* sf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float p = fast_exp2(fmaf(s[v], c2, -lse2[v]));
-      if (need_mask) {
-        const int q = qb + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (q >= N || mykey >= N || (CAUSAL && mykey > q)) p = 0.f;
-      }
-      s[v] = p;
-      dp[v] = p * (dp[v] - dsv[v]);
+    for (int k = 0; k < 2 * NE; ++k) {
+      const int t = k / NE, e = k % NE;
+      dv[e] = E::mma(trrd(base + TB, t, e), pf[t], dv[e]);
+      dk[e] = E::mma(trrd(base, t, e), sf[t], dk[e]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    u32x4 pf[2], sf[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int v0 = 8 * t;
-      pf[t] = u32x4{E::pack(s[v0 + 0], s[v0 + 1]), E::pack(s[v0 + 2], s[v0 + 3]),
-                    E::pack(s[v0 + 4], s[v0 + 5]), E::pack(s[v0 + 6], s[v0 + 7])};
-      sf[t] = u32x4{E::pack(dp[v0 + 0], dp[v0 + 1]), E::pack(dp[v0 + 2], dp[v0 + 3]),
-                    E::pack(dp[v0 + 4], dp[v0 + 5]), E::pack(dp[v0 + 6], dp[v0 + 7])};
+  };
+
+  // Step n: the products of step n+1 interleaved with the elementwise work of step n,
+  // then (if this wave's keys meet the block at all) the accumulation of step n.  The
+  // products of a step past the last, or of one this wave skips, are formed anyway
+  // (reading a valid slot) so that every step has the same branch-free core.
+  auto step = [&](int n, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
+    if (n > 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of step n+1 landed
+      __syncthreads();                                   // everyone's; slot (n-1)%3 is free
     }
-    // dV^T += dO^T P ; dK^T += Q^T dS
+    if (n + 2 < nsteps) dma(n + 2);
+    const int bc = slotp(n), bn = slotp(n + 1);
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 ado = cat(lds_read_tr(dOb + troff + 16 * t * PQ + 64 * e),
-                              lds_read_tr(dOb + troff + (16 * t + 8) * PQ + 64 * e));
-        dv[e] = E::mma(ado, pf[t], dv[e]);
-        const u32x4 aq = cat(lds_read_tr(Qb + troff + 16 * t * PQ + 64 * e),
-                             lds_read_tr(Qb + troff + (16 * t + 8) * PQ + 64 * e));
-        dk[e] = E::mma(aq, sf[t], dk[e]);
+    for (int st = 0; st < NS; ++st) {
+      if (st == 0) {
+        sn = zero16();
+        dpn = zero16();
       }
-    if (step + 1 < nsteps) swrite(buf ^ 1);
-    __syncthreads();
+      sn = E::mma(rowrd(bn, st), kf[st], sn);
+      dpn = E::mma(rowrd(bn + TB, st), vf[st], dpn);
+      elementwise(bc, sc, dpc, (16 * st) / NS, (16 * (st + 1)) / NS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (active(n)) {
+      if (masked(n)) {
+        const int qb = qblock(n);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int q = qb + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (q >= N || mykey >= N || (CAUSAL && mykey > q)) {
+            sc[v] = 0.f;
+            dpc[v] = 0.f;
+          }
+        }
+      }
+      const u32x4 pf[2] = {pack(sc, 0), pack(sc, 1)};
+      const u32x4 sf[2] = {pack(dpc, 0), pack(dpc, 1)};
+      accumulate(bc, pf, sf);
+    }
+  };
+
+  if (nsteps > 0) {
+    dma(0);
+    if (nsteps > 1) dma(1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 sa, pa, sb, pb;   // S and dP of even / odd steps
+  products(0, sa, pa);
+  for (int n = 0; n < nsteps; n += 2) {
+    step(n, sa, pa, sb, pb);
+    if (n + 1 < nsteps) step(n + 1, sb, pb, sa, pa);
   }
 
-  // dK = scale * dK^T^T, dV = dV^T^T, rounded to the input dtype
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T, rounded to the input dtype
   if (mykey < N) {
     unsigned char* dKg = (unsigned char*)a.dk + (kvhead + mykey) * ROWB;
     unsigned char* dVg = (unsigned char*)a.dv + (kvhead + mykey) * ROWB;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * e + 8 * g4 + 4 * hh;
@@ -308,8 +396,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       qf[s] = *(const u32x4*)(qp + 32 * s);
       df[s] = *(const u32x4*)(gp + 32 * s);
     }
-    lse2 = a.lse[qhead + myq] * kLog2e;
-    dsv = a.dsum[qhead + myq];
+    lse2 = a.rowterm[2 * (qhead + myq)];
+    dsv = a.rowterm[2 * (qhead + myq) + 1];
   } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = df[s] = u32x4{0, 0, 0, 0};
@@ -320,7 +408,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  auto dma = [&](int t) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
+  auto dma = [&](int t) __attribute__((always_inline)) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
 
   // per-lane LDS offsets: K and V rows (A operands of S^T, dP^T), K transposed (A of dQ^T)
   const int ka = r32 * PK + 16 * hh;
@@ -333,18 +421,18 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   for (int e = 0; e < NE; ++e) acc[e] = zero16();
 
   // unit u = 32 keys = half (u & 1) of tile u >> 1
-  auto ubase = [&](int u, int half_pitch) {
+  auto ubase = [&](int u, int half_pitch) __attribute__((always_inline)) {
     int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * half_pitch;
     opaque(r);
     return r;
   };
-  auto krow = [&](int kb, int st) { return *(const u32x4*)(lds + kb + ka + 32 * st); };
-  auto vrow = [&](int kb, int st) { return *(const u32x4*)(lds + kb + va + 32 * st); };
-  auto ktr = [&](int kb, int h, int e) {
+  auto krow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + ka + 32 * st); };
+  auto vrow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + va + 32 * st); };
+  auto ktr = [&](int kb, int h, int e) __attribute__((always_inline)) {
     return cat(lds_read_tr(lds + kb + kt + 16 * h * PK + 64 * e), lds_read_tr(lds + kb + kt + (16 * h + 8) * PK + 64 * e));
   };
   // dS of one unit from its S^T and dP^T, packed as the B operand of two 16-key steps
-  auto dsfrom = [&](f32x16& s, const f32x16& dp, int lo, int hi) {
+  auto dsfrom = [&](f32x16& s, const f32x16& dp, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (v >= lo && v < hi) {
@@ -353,7 +441,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
         keep(s[v]);
       }
   };
-  auto pack = [&](const f32x16& s, int h) {
+  auto pack = [&](const f32x16& s, int h) __attribute__((always_inline)) {
     return u32x4{E::pack(s[8 * h + 0], s[8 * h + 1]), E::pack(s[8 * h + 2], s[8 * h + 3]),
                  E::pack(s[8 * h + 4], s[8 * h + 5]), E::pack(s[8 * h + 6], s[8 * h + 7])};
   };
@@ -362,7 +450,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 
   // Unit u < ulast: products of unit u+1 interleaved with the elementwise dS of unit u,
   // then dQ^T += K_u^T dS_u^T.
-  auto step_main = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) {
+  auto step_main = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
     const int kn = ubase(u + 1, PK), vn = ubase(u + 1, PV), kc = ubase(u, PK);
     u32x4 kf = krow(kn, 0), vf = vrow(vn, 0);
     u32x4 pf[2];
@@ -397,7 +485,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   };
 
   // The wave's last unit: diagonal (causal) and/or sequence tail.
-  auto step_last = [&](int u, f32x16& sc, const f32x16& dpc) {
+  auto step_last = [&](int u, f32x16& sc, const f32x16& dpc) __attribute__((always_inline)) {
     const int k0 = u * 32;
     int lim = N - k0 - 4 * hh;
     if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
@@ -413,7 +501,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       for (int e = 0; e < NE; ++e) acc[e] = E::mma(ktr(kc, h, e), pf[h], acc[e]);
   };
 
-  auto step = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) {
+  auto step = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
     if (u < ulast) step_main(u, sc, dpc, sn, dpn);
     else if (u == ulast) step_last(u, sc, dpc);
   };
@@ -436,7 +524,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   }
   const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
   const int J1 = min(ntile, ulast0 / 2);
-  auto tile_start = [&](int j) {
+  auto tile_start = [&](int j) __attribute__((always_inline)) {
     if (j > 0) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();

@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   // ---- HBM -> LDS: tile t of K and V into slot t % 3 ----
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  auto dma = [&](int t) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
+  auto dma = [&](int t) __attribute__((always_inline)) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
 
   // ---- per-lane LDS offsets (plus immediates) ----
   // K (A operand of S^T): row 32c + r32, chunk 2st + hh
@@ -122,30 +122,30 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   // The pipeline works on 32-key units: unit u is half (u & 1) of tile u >> 1.
   // LDS byte offsets of unit u's K rows / V rows for this lane, kept opaque so that
   // every read below is "one register + immediate".
-  auto kbase = [&](int u) {
+  auto kbase = [&](int u) __attribute__((always_inline)) {
     int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PK + ka;
     opaque(r);
     return r;
   };
-  auto vbase = [&](int u) {
+  auto vbase = [&](int u) __attribute__((always_inline)) {
     int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PV + va;
     opaque(r);
     return r;
   };
-  auto kread = [&](int kb, int st) { return *(const u32x4*)(lds + kb + 32 * st); };
-  auto vread = [&](int vb, int h, int e) {
+  auto kread = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + 32 * st); };
+  auto vread = [&](int vb, int h, int e) __attribute__((always_inline)) {
     return cat(lds_read_tr(lds + vb + 16 * h * PV + 64 * e), lds_read_tr(lds + vb + (16 * h + 8) * PV + 64 * e));
   };
 
   // Softmax pieces on the scores s of one unit (in log2 units after * c2).
-  auto rowmax = [&](const f32x16& s) {
+  auto rowmax = [&](const f32x16& s) __attribute__((always_inline)) {
     float mx = s[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
     return mx;
   };
   // new reference from the unit's row max; returns alpha = exp2(old - new), sets mref
-  auto newref = [&](float mx, bool& raise, float& mref) {
+  auto newref = [&](float mx, bool& raise, float& mref) __attribute__((always_inline)) {
     mx *= c2;
     raise = mx > mr + TAU;
     const float mnew = raise ? mx : mr;
@@ -154,11 +154,11 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     mr = mnew;
     return alpha;
   };
-  auto packp = [&](const f32x16& s, int h) {
+  auto packp = [&](const f32x16& s, int h) __attribute__((always_inline)) {
     return u32x4{E::pack(s[8 * h + 0], s[8 * h + 1]), E::pack(s[8 * h + 2], s[8 * h + 3]),
                  E::pack(s[8 * h + 4], s[8 * h + 5]), E::pack(s[8 * h + 6], s[8 * h + 7])};
   };
-  auto rescale = [&](float alpha) {
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   // Unit u (u < ulast), hand-scheduled.  S-phase: NS slots, each one MFMA of S_{u+1}
   // plus a share of the softmax of unit u; PV-phase: 2*NE slots, each one MFMA of
   // O^T += V^T P plus two adds of the row sum.  LDS reads run two slots ahead.
-  auto step_main = [&](int u, f32x16& sc, f32x16& sn) {
+  auto step_main = [&](int u, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
     const int kb = kbase(u + 1);
     const int vb = vbase(u);
     u32x4 kf[NS];
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   };
 
   // The wave's last unit: diagonal (causal) and/or sequence tail; no next unit.
-  auto step_last = [&](int u, f32x16& sc) {
+  auto step_last = [&](int u, f32x16& sc) __attribute__((always_inline)) {
     const int k0 = u * 32;
     int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
     if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     l_run = fmaf(l_run, alpha, rs);
   };
 
-  auto step = [&](int u, f32x16& sc, f32x16& sn) {
+  auto step = [&](int u, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
     if (u < ulast) step_main(u, sc, sn);
     else if (u == ulast) step_last(u, sc);
   };
@@ -294,7 +294,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   // Tiles [0, J1): every wave has both units ahead of its last one (branch-free loop).
   const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;   // the smallest ulast
   const int J1 = min(ntile, ulast0 / 2);
-  auto tile_start = [&](int j) {
+  auto tile_start = [&](int j) __attribute__((always_inline)) {
     if (j > 0) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile j+1 landed
       __syncthreads();                                   // everyone's; slot (j-1)%3 is free
