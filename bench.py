@@ -56,8 +56,10 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "fwd": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h"],
-    "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h"],
+    "fwd": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
+            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
+    "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
+            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
@@ -247,7 +249,7 @@ def main():
                       "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12}}
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
     if not args.fwd_only:
-        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_main_kernel + bwd_dq_kernel", "launches": 3,
+        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "launches": 3,
                          "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12}
         passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
     def roofline(kind):
