@@ -20,7 +20,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-munsafe-fp-atomics",            # hardware float atomics for the dQ accumulator
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}",

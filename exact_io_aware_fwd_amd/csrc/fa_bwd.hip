@@ -16,13 +16,15 @@
 //
 //  1. row terms: LSE_i * log2(e) and D_i = sum_k dO_ik O_ik in fp32, as pairs;
 //  2. dQ pass: one workgroup per (batch, head, 32*NW-query block), the forward's
-//     structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K, V tiles
-//     streamed through LDS; P = exp2(S*scale*log2e - LSE*log2e),
+//     structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K (XOR-
+//     swizzled: read by rows and transposed), V tiles streamed through LDS;
+//     P = exp2(S*scale*log2e - LSE*log2e),
 //     dS = P * (dP - D) in registers, dQ^T += K^T dS^T (K read transposed);
 //  3. dK/dV pass: one workgroup per (batch, K/V head, 128-key block); each of the
 //     4 waves owns 32 keys, holds their K and V in VGPRs and dK^T, dV^T in
 //     accumulators across all query heads of the group and all query blocks (from
-//     the diagonal when causal).  Q, dO and the row terms of each 32-query step go
+//     the diagonal when causal; query blocks descending, heads inner, so that
+//     concurrent workgroups share Q/dO tiles in L2).  Q, dO and the row terms of each 32-query step go
 //     HBM -> LDS directly (three slots, two steps in flight).  Per step:
 //     S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P, dK^T += Q^T dS (Q^T,
 //     dO^T read transposed from LDS); the products of step n+1 are interleaved
@@ -60,17 +62,6 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
 }
 
 // ---- 3. dK, dV per key block ---------------------------------------------------------
-// XOR on the 16-byte chunk index of row r of a Q/dO tile in LDS.  The tiles are read
-// both by rows (16 bytes per lane, 16 consecutive rows) and transposed
-// (ds_read_b64_tr_b16, 8 bytes per lane from 4 consecutive rows); with this XOR
-// both patterns hit distinct banks (measured free of bank conflicts), and each
-// address is a lane constant XOR an instruction constant.
-template <int CH>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
-}
-
 // Q rows, dO rows (TB bytes each, 16-byte chunks XOR-swizzled by soff) and the
 // (LSE*log2e, D) row pairs of one query block into an LDS slot, straight from HBM.
 // `rows` rows remain from the block's first row on; rows past them arrive as zeros.
@@ -162,8 +153,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const int per_head = nqb - iq0;
   const int nsteps = G * per_head;
 
-  // ---- HBM -> LDS: step n (query head hkv*G + n / per_head, query block
-  // iq0 + n % per_head) into slot n % 3.  Tile load nn = wave + NW*i covers slot bytes
+  // ---- HBM -> LDS: step n into slot n % 3.  Tile load nn = wave + NW*i covers slot bytes
   // [1024nn, 1024nn+1024) (Q tile, then dO tile); lane's 16 bytes come from byte soff[i]
   // of the tile's rows (chunks XOR-swizzled).  Rows past N arrive as zeros.
   int soff[LI];
@@ -173,34 +163,25 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     const int row = (nn % TI) * RPI + lane / CH;
     soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
   }
+  // step n: query block nqb-1 - n/G (descending, so that the workgroups of a group walk
+  // the same Q/dO tiles at the same time), query head hkv*G + n%G
   auto dma = [&](int n) __attribute__((always_inline)) {
-    const int g = n / per_head;
-    const int qb = (iq0 + n - g * per_head) * BQ;
+    const int g = n % G;
+    const int qb = (nqb - 1 - n / G) * BQ;
     const size_t qrow = (size_t)(b * a.Hq + hkv * G + g) * (size_t)N + qb;
     dkdv_load_step<ROWB, TI, LI, NW, TB>(a, qrow, N - qb, wave, lane, soff, lds + (n % 3) * SLOT);
   };
 
-  // ---- per-lane LDS addresses ----
-  // rows (A of S = Q K^T and dP = dO V^T): row r32, chunk 2st + hh
+  // ---- per-lane LDS addresses (swizzled tiles) ----
+  using SO = SwzOffsets<ROWB>;
   int rowa[NS];
-  {
-    const int a0 = r32 * ROWB + ((hh ^ swz<CH>(r32)) << 4);
 #pragma unroll
-    for (int st = 0; st < NS; ++st) rowa[st] = a0 ^ (st << 5);
-  }
-  // transposed (A of dV^T = dO^T P and dK^T = Q^T dS): rows 16t + 8u + R, elements 32e + 16x + 4y
+  for (int st = 0; st < NS; ++st) rowa[st] = SO::rows_a0(lane) ^ (st << 5);
   int tra[2 * NE];
-  {
-    const int R = 4 * hh + ((lane & 15) >> 2), x = (lane >> 4) & 1, y = lane & 3;
-    int lp;
-    if constexpr (CH == 16) lp = (2 * x) ^ (y >> 1) ^ ((R & 3) << 2) ^ hh;
-    else lp = (2 * x) ^ (y >> 1) ^ (((R >> 1) & 3) << 1);
-    const int al = R * ROWB + (lp << 4) + 8 * (y & 1);
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
+  for (int e = 0; e < NE; ++e)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) tra[2 * e + u] = al ^ ((CH == 16 ? ((4 * e) ^ (2 * u)) : ((4 * e) ^ u)) << 4);
-  }
+    for (int u = 0; u < 2; ++u) tra[2 * e + u] = SO::tr_lane(lane) ^ SO::tr_inst(e, u);
   auto slotp = [&](int n) __attribute__((always_inline)) {
     int r = (n % 3) * SLOT;
     opaque(r);
@@ -221,10 +202,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const float c2 = a.scale_log2;
 
   // step n's query block and head
-  auto qblock = [&](int n) __attribute__((always_inline)) {
-    const int g = n / per_head;
-    return (iq0 + n - g * per_head) * BQ;
-  };
+  auto qblock = [&](int n) __attribute__((always_inline)) { return (nqb - 1 - n / G) * BQ; };
   // wave activity and masking for step n (all wave-uniform)
   auto active = [&](int n) __attribute__((always_inline)) { return n < nsteps && (!CAUSAL || kw <= qblock(n)); };
   auto masked = [&](int n) __attribute__((always_inline)) {
@@ -357,9 +335,10 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   constexpr int BR = 32 * NW;           // query rows per workgroup
   constexpr int BC = 64;                // keys per tile
   constexpr int ROWB = D * 2;
-  constexpr int PK = ROWB + 64;         // K rows: read as rows (S^T) and transposed (dQ^T)
-  constexpr int PV = ROWB + 16;         // V rows: read as rows (dP^T)
-  using Tiles = TilePair<ROWB, PK, PV, NW>;
+  constexpr int PK = ROWB;              // K rows: read by rows (S^T) and transposed (dQ^T): swizzled
+  constexpr int PV = ROWB + 16;         // V rows: read by rows (dP^T): padded
+  using Tiles = TilePair<ROWB, PK, PV, NW, true>;
+  using SO = SwzOffsets<ROWB>;
   constexpr int KBYTES = Tiles::ABYTES;
   constexpr int SLOT = Tiles::SLOT;
   constexpr int IPW = Tiles::IPW;
@@ -410,10 +389,17 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   Tiles::offsets(wave, lane, doff);
   auto dma = [&](int t) __attribute__((always_inline)) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
 
-  // per-lane LDS offsets: K and V rows (A operands of S^T, dP^T), K transposed (A of dQ^T)
-  const int ka = r32 * PK + 16 * hh;
+  // per-lane LDS offsets: K rows (swizzled) and V rows (A operands of S^T, dP^T), K
+  // transposed (A of dQ^T, swizzled)
+  int ka[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) ka[st] = SO::rows_a0(lane) ^ (st << 5);
+  int kt[2 * NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kt[2 * e + u] = SO::tr_lane(lane) ^ SO::tr_inst(e, u);
   const int va = KBYTES + r32 * PV + 16 * hh;
-  const int kt = (4 * hh + ((lane & 15) >> 2)) * PK + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   const float c2 = a.scale_log2;
   f32x16 acc[NE];
@@ -426,10 +412,10 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     opaque(r);
     return r;
   };
-  auto krow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + ka + 32 * st); };
+  auto krow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + ka[st]); };
   auto vrow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + va + 32 * st); };
   auto ktr = [&](int kb, int h, int e) __attribute__((always_inline)) {
-    return cat(lds_read_tr(lds + kb + kt + 16 * h * PK + 64 * e), lds_read_tr(lds + kb + kt + (16 * h + 8) * PK + 64 * e));
+    return cat(lds_read_tr(lds + kb + 16 * h * PK + kt[2 * e]), lds_read_tr(lds + kb + (16 * h + 8) * PK + kt[2 * e + 1]));
   };
   // dS of one unit from its S^T and dP^T, packed as the B operand of two 16-key steps
   auto dsfrom = [&](f32x16& s, const f32x16& dp, int lo, int hi) __attribute__((always_inline)) {
