@@ -13,6 +13,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+# Per-source flags.  The backward kernels keep their long-lived accumulators in AGPRs
+# through inline-asm MFMAs; every other MFMA is asked to write VGPRs, which is where
+# the elementwise code reads S and dP (otherwise the compiler may place those results
+# in AGPRs and copy them back on every step).
+SOURCE_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -28,7 +33,7 @@ FLAGS = [
 
 
 def _compile(src: str, out: str, extra: list[str]) -> tuple[str, int, str]:
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     p = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature; that note is harmless
     err = "\n".join(l for l in p.stderr.splitlines() if "packed-fp32-ops" not in l)

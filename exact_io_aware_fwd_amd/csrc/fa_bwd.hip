@@ -29,22 +29,36 @@
 //     S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P, dK^T += Q^T dS (Q^T,
 //     dO^T read transposed from LDS); the products of step n+1 are interleaved
 //     with the elementwise work of step n.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
 namespace fa {
 
-// ---- 1. row terms: (LSE_i * log2 e, D_i = sum_k dO_ik O_ik) per query row ------------
+// Row-term layout (the workspace): per (batch, query head), per block of 32 query rows,
+// 32 floats LSE_i * log2(e) then 32 floats -D_i; rows of the last block past N hold 0.
+__host__ __device__ inline long long rowterm_index(long long bh, int nb32, int row) {
+  return (bh * nb32 + row / 32) * 64 + (row & 31);
+}
+
+// ---- 1. row terms: LSE_i * log2 e and -D_i = -sum_k dO_ik O_ik per query row ----------
 template <class Tag, int D>
-__global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long long rows) {
+__global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long long prows) {
   using E = Elt<Tag>;
   constexpr int TPR = D / 8;   // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int N = a.N;
+  const int nb32 = (N + 31) / 32;
+  const long long p = (long long)blockIdx.x * RPB + threadIdx.x / TPR;   // padded row
+  const long long bh = p / (32LL * nb32);
+  const int r = (int)(p - bh * 32LL * nb32);
   const int part = threadIdx.x % TPR;
+  const bool real = p < prows && r < N;
+  const long long row = bh * N + r;
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const u32x4 o4 = *(const u32x4*)((const unsigned char*)a.o + (row * D + part * 8) * 2);
     const u32x4 g4 = *(const u32x4*)((const unsigned char*)a.dout + (row * D + part * 8) * 2);
 #pragma unroll
@@ -55,44 +69,42 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && part == 0) {
-    a.rowterm[2 * row] = a.lse[row] * kLog2e;
-    a.rowterm[2 * row + 1] = acc;
+  if (p < prows && part == 0) {
+    const long long t = rowterm_index(bh, nb32, r);
+    a.rowterm[t] = real ? a.lse[row] * kLog2e : 0.f;
+    a.rowterm[t + 32] = real ? -acc : 0.f;
   }
 }
 
 // ---- 3. dK, dV per key block ---------------------------------------------------------
-// Q rows, dO rows (TB bytes each, 16-byte chunks XOR-swizzled by soff) and the
-// (LSE*log2e, D) row pairs of one query block into an LDS slot, straight from HBM.
-// `rows` rows remain from the block's first row on; rows past them arrive as zeros.
+// Q rows and dO rows of one 32-query step (XOR-swizzled chunks: lane's 16 bytes of
+// tile load i land where soff[i] says) and the step's 256 bytes of row terms, from HBM
+// straight into an LDS slot.  qh/gh/rh are the head's first Q row, dO row and row-term
+// block; the buffer ranges end at the head's row N, so rows past it arrive as zeros.
 // (A free function: the host pass of the compiler mishandles these builtins inside a
 // capturing lambda.)
 template <int ROWB, int TI, int LI, int NW, int TB>
-__device__ __forceinline__ void dkdv_load_step(const BwdArgs& a, size_t qrow, int rows, int wave, int lane,
-                                               const int* soff, unsigned char* slot) {
-  const int bytes = rows * ROWB;
-  const __amdgpu_buffer_rsrc_t rq =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.q + qrow * ROWB), (short)0, bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const unsigned char*)a.dout + qrow * ROWB), (short)0, bytes, 0x00020000);
+__device__ __forceinline__ void dkdv_dma(const unsigned char* qh, const unsigned char* gh, const float* rh,
+                                         int hbytes, int rbytes, int qoff, int roff, int wave, int lane,
+                                         const int* soff, unsigned char* slot) {
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qh, (short)0, hbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)gh, (short)0, hbytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < LI; ++i) {
-    const int nn = wave + NW * i;
-    if (nn < TI)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lvoid*)(slot + nn * 1024), 16, soff[i], 0, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lvoid*)(slot + nn * 1024), 16, soff[i], 0, 0, 0);
+    const int nn = wave + NW * i;   // tile load: Q for i < LI/2, dO after
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(i < LI / 2 ? rq : rd, (lvoid*)(slot + nn * 1024), 16, soff[i] + qoff,
+                                             0, 0, 0);
   }
   if (wave == 0) {
-    const __amdgpu_buffer_rsrc_t rr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.rowterm + 2 * qrow), (short)0, rows * 8, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lvoid*)(slot + 2 * TB), 4, lane * 4, 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)rh, (short)0, rbytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lvoid*)(slot + 2 * TB), 4, lane * 4 + roff, 0, 0, 0);
   }
 }
 
 template <class Tag, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
+  using A = AccMma<Tag>;
   constexpr int NW = 4;
   constexpr int BKV = 32 * NW;        // keys per workgroup; wave w owns keys 32w .. 32w+31
   constexpr int BQ = 32;              // queries per step
@@ -103,11 +115,20 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int TB = BQ * ROWB;       // bytes of one Q (or dO) tile
   constexpr int TI = TB / 1024;       // wave-wide 16-byte-per-lane loads per tile
   constexpr int RPI = 1024 / ROWB;    // rows per such load
-  constexpr int LI = (2 * TI + NW - 1) / NW;
-  constexpr int SLOT = 2 * TB + BQ * 8;   // Q tile, dO tile, (LSE*log2e, D) pairs
-  static_assert(2 * TI % NW == 0, "tile loads split evenly");
+  constexpr int LI = 2 * TI / NW;     // tile loads per wave per step
+  constexpr int RT = 2 * TB;          // row terms in the slot: 32 x LSE*log2e, 32 x -D
+  constexpr int SLOT = 2 * TB + 256;
+  static_assert(TI % NW == 0, "each wave loads whole Q / dO halves");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
+  // Three slots as distinct LDS objects: with every step's slot known at compile time,
+  // the compiler can tell that the loads into one slot do not touch the slots being
+  // read, and does not make those reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -148,14 +169,15 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     for (int s = 0; s < NS; ++s) kf[s] = vf[s] = u32x4{0, 0, 0, 0};
   }
 
-  const int iq0 = CAUSAL ? k0 / BQ : 0;
-  const int nqb = (N + BQ - 1) / BQ;
-  const int per_head = nqb - iq0;
+  // Steps: for each query head of the group, query blocks from the last down to the
+  // first one that meets these keys (the key block's own start when causal).
+  const int nb32 = (N + 31) / 32;
+  const int qtop = (nb32 - 1) * BQ;
+  const int qlo = CAUSAL ? k0 : 0;
+  const int per_head = (qtop - qlo) / BQ + 1;
   const int nsteps = G * per_head;
 
-  // ---- HBM -> LDS: step n into slot n % 3.  Tile load nn = wave + NW*i covers slot bytes
-  // [1024nn, 1024nn+1024) (Q tile, then dO tile); lane's 16 bytes come from byte soff[i]
-  // of the tile's rows (chunks XOR-swizzled).  Rows past N arrive as zeros.
+  // ---- HBM -> LDS (step n into slot n % 3), driven by a cursor over (head, block) ----
   int soff[LI];
 #pragma unroll
   for (int i = 0; i < LI; ++i) {
@@ -163,13 +185,21 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     const int row = (nn % TI) * RPI + lane / CH;
     soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
   }
-  // step n: query block nqb-1 - n/G (descending, so that the workgroups of a group walk
-  // the same Q/dO tiles at the same time), query head hkv*G + n%G
-  auto dma = [&](int n) __attribute__((always_inline)) {
-    const int g = n % G;
-    const int qb = (nqb - 1 - n / G) * BQ;
-    const size_t qrow = (size_t)(b * a.Hq + hkv * G + g) * (size_t)N + qb;
-    dkdv_load_step<ROWB, TI, LI, NW, TB>(a, qrow, N - qb, wave, lane, soff, lds + (n % 3) * SLOT);
+  const size_t qhead0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
+  const unsigned char* dq_h = (const unsigned char*)a.q + qhead0 * ROWB;
+  const unsigned char* dg_h = (const unsigned char*)a.dout + qhead0 * ROWB;
+  const float* dr_h = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
+  const int hbytes = N * ROWB, rbytes = nb32 * 256;
+  int dqb = qtop;   // query block of the next step to load
+  auto dma_next = [&](unsigned char* sl) __attribute__((always_inline)) {
+    dkdv_dma<ROWB, TI, LI, NW, TB>(dq_h, dg_h, dr_h, hbytes, rbytes, dqb * ROWB, dqb * 8, wave, lane, soff, sl);
+    dqb -= BQ;
+    if (dqb < qlo) {
+      dqb = qtop;
+      dq_h += hbytes;
+      dg_h += hbytes;
+      dr_h += nb32 * 64;
+    }
   };
 
   // ---- per-lane LDS addresses (swizzled tiles) ----
@@ -182,132 +212,159 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   for (int e = 0; e < NE; ++e)
 #pragma unroll
     for (int u = 0; u < 2; ++u) tra[2 * e + u] = SO::tr_lane(lane) ^ SO::tr_inst(e, u);
-  auto slotp = [&](int n) __attribute__((always_inline)) {
-    int r = (n % 3) * SLOT;
-    opaque(r);
-    return r;
+  auto rowrd = [&](const unsigned char* sl, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + rowa[st]);
   };
-  auto rowrd = [&](int base, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + base + rowa[st]); };
-  auto trrd = [&](int base, int t, int e) __attribute__((always_inline)) {
-    return cat(lds_read_tr(lds + base + 16 * t * ROWB + tra[2 * e]),
-               lds_read_tr(lds + base + (16 * t + 8) * ROWB + tra[2 * e + 1]));
+  auto trrd = [&](const unsigned char* sl, int t, int e) __attribute__((always_inline)) {
+    return cat(lds_read_tr(sl + 16 * t * ROWB + tra[2 * e]), lds_read_tr(sl + (16 * t + 8) * ROWB + tra[2 * e + 1]));
+  };
+  // row terms of this lane's 16 rows q = 8(v/4) + 4hh + v%4: four 16-byte reads
+  auto rt4 = [&](const unsigned char* sl, int off, int j) __attribute__((always_inline)) {
+    return *(const f32x4*)(sl + RT + off + (8 * j + 4 * hh) * 4);
+  };
+  auto rt16 = [&](const unsigned char* sl, int off) __attribute__((always_inline)) {
+    f32x16 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 t = rt4(sl, off, j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[4 * j + i] = t[i];
+    }
+    return r;
   };
 
   f32x16 dk[NE], dv[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) {
-    dk[e] = zero16();
-    dv[e] = zero16();
-  }
+  acc_init(dk);
+  acc_init(dv);
   const float c2 = a.scale_log2;
 
-  // step n's query block and head
-  auto qblock = [&](int n) __attribute__((always_inline)) { return (nqb - 1 - n / G) * BQ; };
-  // wave activity and masking for step n (all wave-uniform)
-  auto active = [&](int n) __attribute__((always_inline)) { return n < nsteps && (!CAUSAL || kw <= qblock(n)); };
-  auto masked = [&](int n) __attribute__((always_inline)) {
-    const int qb = qblock(n);
-    return (CAUSAL && kw == qb) || qb + BQ > N || kw + 32 > N;
-  };
-
-  // S = Q K^T and dP = dO V^T of step n
-  auto products = [&](int n, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
-    const int base = slotp(n);
-    s = zero16();
-    dp = zero16();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      s = E::mma(rowrd(base, st), kf[st], s);
-      dp = E::mma(rowrd(base + TB, st), vf[st], dp);
-    }
-  };
-  // P and dS of step n in place (s -> p, dp -> ds) for elements [lo, hi); rows q = 8(v/4) + 4hh + v%4
-  auto elementwise = [&](int base, f32x16& s, f32x16& dp, int lo, int hi) __attribute__((always_inline)) {
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      if (4 * a4 + 3 < lo || 4 * a4 >= hi) continue;
-      const f32x4 t0 = *(const f32x4*)(lds + base + 2 * TB + (8 * a4 + 4 * hh) * 8);
-      const f32x4 t1 = *(const f32x4*)(lds + base + 2 * TB + (8 * a4 + 4 * hh) * 8 + 16);
-      const float l2[4] = {t0[0], t0[2], t1[0], t1[2]}, dd[4] = {t0[1], t0[3], t1[1], t1[3]};
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int v = 4 * a4 + bb;
-        if (v < lo || v >= hi) continue;
-        const float p = fast_exp2(fmaf(s[v], c2, -l2[bb]));
-        s[v] = p;
-        dp[v] = p * (dp[v] - dd[bb]);
-        keep(s[v]);
-        keep(dp[v]);
-      }
-    }
-  };
   auto pack = [&](const f32x16& s, int t) __attribute__((always_inline)) {
     return u32x4{E::pack(s[8 * t + 0], s[8 * t + 1]), E::pack(s[8 * t + 2], s[8 * t + 3]),
                  E::pack(s[8 * t + 4], s[8 * t + 5]), E::pack(s[8 * t + 6], s[8 * t + 7])};
   };
-  // dV^T += dO^T P, dK^T += Q^T dS for step n
-  auto accumulate = [&](int base, const u32x4* pf, const u32x4* sf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < 2 * NE; ++k) {
-      const int t = k / NE, e = k % NE;
-      dv[e] = E::mma(trrd(base + TB, t, e), pf[t], dv[e]);
-      dk[e] = E::mma(trrd(base, t, e), sf[t], dk[e]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
-  // Step n: the products of step n+1 interleaved with the elementwise work of step n,
-  // then (if this wave's keys meet the block at all) the accumulation of step n.  The
-  // products of a step past the last, or of one this wave skips, are formed anyway
-  // (reading a valid slot) so that every step has the same branch-free core.
-  auto step = [&](int n, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
+  // Step n (slot J % 3; S, dP of step n in (sc, dpc), of step n+1 formed into (sn, dpn)):
+  //   sync; load step n+2;
+  //   NS sub-steps: [elementwise of step n: P = exp2(S*c - LSE2), dS = P * (dP - D)]
+  //                 [S_{n+1} += Q K^T, dP_{n+1} += dO V^T for one k-step]
+  //   if the step meets this wave's keys: (diagonal: mask) pack; dV^T += dO^T P,
+  //   dK^T += Q^T dS.
+  // dP_{n+1} starts from -D, so dP - D comes out of the MFMA.  The products of a step
+  // past the last are formed anyway from a valid slot and never used.
+  int cqb = qtop;   // query block of the current step
+  f32x16 l2n;       // LSE*log2e of the current step's rows
+  auto step = [&](auto Jc, int n, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
+    constexpr int J = decltype(Jc)::value;
+    unsigned char* const bc = slot(J % 3);
+    unsigned char* const bn = slot((J + 1) % 3);
+    unsigned char* const bl = slot((J + 2) % 3);
     if (n > 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of step n+1 landed
-      __syncthreads();                                   // everyone's; slot (n-1)%3 is free
+      wait_loads();      // this wave's loads of step n+1 landed
+      __syncthreads();   // everyone's; everyone is done with slot (n-1)%3
     }
-    if (n + 2 < nsteps) dma(n + 2);
-    const int bc = slotp(n), bn = slotp(n + 1);
+    if (n + 2 < nsteps) dma_next(bl);
+    const f32x16 l2 = l2n;
+    const f32x16 nd = rt16(bn, 128);
+    u32x4 qa = rowrd(bn, 0), ga = rowrd(bn + TB, 0);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      if (st == 0) {
-        sn = zero16();
-        dpn = zero16();
+#pragma unroll
+      for (int v = (16 * st) / NS; v < (16 * (st + 1)) / NS; ++v) {
+        const float p = fast_exp2(fmaf(sc[v], c2, -l2[v]));
+        sc[v] = p;
+        dpc[v] = p * dpc[v];
+        keep(sc[v]);
+        keep(dpc[v]);
       }
-      sn = E::mma(rowrd(bn, st), kf[st], sn);
-      dpn = E::mma(rowrd(bn + TB, st), vf[st], dpn);
-      elementwise(bc, sc, dpc, (16 * st) / NS, (16 * (st + 1)) / NS);
+      const u32x4 qc = qa, gc = ga;
+      if (st + 1 < NS) {
+        qa = rowrd(bn, st + 1);
+        ga = rowrd(bn + TB, st + 1);
+      }
+      sn = E::mma(qc, kf[st], st == 0 ? zero16() : sn);
+      dpn = E::mma(gc, vf[st], st == 0 ? nd : dpn);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (active(n)) {
-      if (masked(n)) {
-        const int qb = qblock(n);
+    l2n = rt16(bn, 0);
+    const bool active = !CAUSAL || cqb >= kw;
+    if (active) {
+      if (CAUSAL && cqb == kw) {
+        // diagonal block: query 8(v/4) + 4hh + v%4 sees key r32 only if r32 <= query
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int q = qb + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (q >= N || mykey >= N || (CAUSAL && mykey > q)) {
+        for (int v = 0; v < 16; ++v)
+          if (r32 > 8 * (v >> 2) + 4 * hh + (v & 3)) {
             sc[v] = 0.f;
             dpc[v] = 0.f;
           }
-        }
       }
       const u32x4 pf[2] = {pack(sc, 0), pack(sc, 1)};
       const u32x4 sf[2] = {pack(dpc, 0), pack(dpc, 1)};
-      accumulate(bc, pf, sf);
+      keep(pf[0]);
+      keep(pf[1]);
+      keep(sf[0]);
+      keep(sf[1]);
+      u32x4 ta = trrd(bc + TB, 0, 0), tb = trrd(bc, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NE; ++k) {
+        const int t = k / NE, e = k % NE;
+        const u32x4 tc = ta, td = tb;
+        if (k + 1 < 2 * NE) {
+          ta = trrd(bc + TB, (k + 1) / NE, (k + 1) % NE);
+          tb = trrd(bc, (k + 1) / NE, (k + 1) % NE);
+        }
+        if (k == 0) {
+          A::mma_fresh(dv[e], tc, pf[t]);
+          A::mma_fresh(dk[e], td, sf[t]);
+        } else {
+          A::mma(dv[e], tc, pf[t]);
+          A::mma(dk[e], td, sf[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    cqb -= BQ;
+    if (cqb < qlo) cqb = qtop;
   };
 
   if (nsteps > 0) {
-    dma(0);
-    if (nsteps > 1) dma(1);
+    dma_next(slot0);
+    if (nsteps > 1) dma_next(slot1);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_loads();
   __syncthreads();
   f32x16 sa, pa, sb, pb;   // S and dP of even / odd steps
-  products(0, sa, pa);
-  for (int n = 0; n < nsteps; n += 2) {
-    step(n, sa, pa, sb, pb);
-    if (n + 1 < nsteps) step(n + 1, sb, pb, sa, pa);
+  {
+    const f32x16 nd = rt16(slot0, 128);
+    sa = zero16();
+    pa = nd;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      sa = E::mma(rowrd(slot0, st), kf[st], sa);
+      pa = E::mma(rowrd(slot0 + TB, st), vf[st], pa);
+    }
+    l2n = rt16(slot0, 0);
   }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  for (int n = 0; n < nsteps; n += 6) {
+    step(I0{}, n, sa, pa, sb, pb);
+    if (n + 1 >= nsteps) break;
+    step(I1{}, n + 1, sb, pb, sa, pa);
+    if (n + 2 >= nsteps) break;
+    step(I2{}, n + 2, sa, pa, sb, pb);
+    if (n + 3 >= nsteps) break;
+    step(I3{}, n + 3, sb, pb, sa, pa);
+    if (n + 4 >= nsteps) break;
+    step(I4{}, n + 4, sa, pa, sb, pb);
+    if (n + 5 >= nsteps) break;
+    step(I5{}, n + 5, sb, pb, sa, pa);
+  }
+  acc_drain(dk);
+  acc_drain(dv);
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T, rounded to the input dtype
   if (mykey < N) {
@@ -332,6 +389,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 template <class Tag, int D, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
+  using A = AccMma<Tag>;
   constexpr int BR = 32 * NW;           // query rows per workgroup
   constexpr int BC = 64;                // keys per tile
   constexpr int ROWB = D * 2;
@@ -345,7 +403,14 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   constexpr int NE = D / 32;            // 32-row blocks of dQ^T
   constexpr int NS = D / 16;            // k-steps of S^T and dP^T
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
+  // Three slots as distinct LDS objects (see the dK/dV pass): tile j uses slot j % 3,
+  // known at compile time in the 3-tile unrolled loops.
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -366,7 +431,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 
   // Q^T and dO^T as B operands: lane holds row myq, elements 16s + 8hh .. +7
   u32x4 qf[NS], df[NS];
-  float lse2 = 0.f, dsv = 0.f;
+  float lse2 = 0.f, negd = 0.f;
   if (myq < N) {
     const unsigned char* qp = (const unsigned char*)a.q + (qhead + myq) * ROWB + 16 * hh;
     const unsigned char* gp = (const unsigned char*)a.dout + (qhead + myq) * ROWB + 16 * hh;
@@ -375,19 +440,26 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       qf[s] = *(const u32x4*)(qp + 32 * s);
       df[s] = *(const u32x4*)(gp + 32 * s);
     }
-    lse2 = a.rowterm[2 * (qhead + myq)];
-    dsv = a.rowterm[2 * (qhead + myq) + 1];
+    const long long t = rowterm_index((long long)b * a.Hq + hq, (N + 31) / 32, myq);
+    lse2 = a.rowterm[t];
+    negd = a.rowterm[t + 32];
   } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = df[s] = u32x4{0, 0, 0, 0};
   }
+  // dP^T of every unit starts from -D (this lane's query), so dP - D comes out of the MFMA
+  f32x16 ndv;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndv[i] = negd;
 
   const int nkv = (N + BC - 1) / BC;
   const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
 
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  auto dma = [&](int t) __attribute__((always_inline)) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
+  auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
+    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+  };
 
   // per-lane LDS offsets: K rows (swizzled) and V rows (A operands of S^T, dP^T), K
   // transposed (A of dQ^T, swizzled)
@@ -399,31 +471,30 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   for (int e = 0; e < NE; ++e)
 #pragma unroll
     for (int u = 0; u < 2; ++u) kt[2 * e + u] = SO::tr_lane(lane) ^ SO::tr_inst(e, u);
-  const int va = KBYTES + r32 * PV + 16 * hh;
+  const int va = r32 * PV + 16 * hh;
 
   const float c2 = a.scale_log2;
   f32x16 acc[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = zero16();
+  acc_init(acc);
 
-  // unit u = 32 keys = half (u & 1) of tile u >> 1
-  auto ubase = [&](int u, int half_pitch) __attribute__((always_inline)) {
-    int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * half_pitch;
-    opaque(r);
-    return r;
+  // unit = 32 keys: half h of the tile in slot sl
+  auto krow = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + h * 32 * PK + ka[st]);
   };
-  auto krow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + ka[st]); };
-  auto vrow = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + va + 32 * st); };
-  auto ktr = [&](int kb, int h, int e) __attribute__((always_inline)) {
-    return cat(lds_read_tr(lds + kb + 16 * h * PK + kt[2 * e]), lds_read_tr(lds + kb + (16 * h + 8) * PK + kt[2 * e + 1]));
+  auto vrow = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + KBYTES + h * 32 * PV + va + 32 * st);
   };
-  // dS of one unit from its S^T and dP^T, packed as the B operand of two 16-key steps
+  auto ktr = [&](const unsigned char* sl, int h, int t, int e) __attribute__((always_inline)) {
+    return cat(lds_read_tr(sl + (32 * h + 16 * t) * PK + kt[2 * e]),
+               lds_read_tr(sl + (32 * h + 16 * t + 8) * PK + kt[2 * e + 1]));
+  };
+  // dS of one unit from its S^T and dP^T - D
   auto dsfrom = [&](f32x16& s, const f32x16& dp, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (v >= lo && v < hi) {
         const float p = fast_exp2(fmaf(s[v], c2, -lse2));
-        s[v] = p * (dp[v] - dsv);
+        s[v] = p * dp[v];
         keep(s[v]);
       }
   };
@@ -431,102 +502,107 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     return u32x4{E::pack(s[8 * h + 0], s[8 * h + 1]), E::pack(s[8 * h + 2], s[8 * h + 3]),
                  E::pack(s[8 * h + 4], s[8 * h + 5]), E::pack(s[8 * h + 6], s[8 * h + 7])};
   };
+  auto accumulate = [&](const unsigned char* sl, int h, const u32x4* pf) __attribute__((always_inline)) {
+    u32x4 tf = ktr(sl, h, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * NE; ++k) {
+      const int t = k / NE, e = k % NE;
+      const u32x4 cur = tf;
+      if (k + 1 < 2 * NE) tf = ktr(sl, h, (k + 1) / NE, (k + 1) % NE);
+      if (k == 0) A::mma_fresh(acc[e], cur, pf[t]);
+      else A::mma(acc[e], cur, pf[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  const int ulast = (CAUSAL ? min(qw + 31, N - 1) : N - 1) / 32;
-
-  // Unit u < ulast: products of unit u+1 interleaved with the elementwise dS of unit u,
-  // then dQ^T += K_u^T dS_u^T.
-  auto step_main = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
-    const int kn = ubase(u + 1, PK), vn = ubase(u + 1, PV), kc = ubase(u, PK);
-    u32x4 kf = krow(kn, 0), vf = vrow(vn, 0);
+  // Unit u in (sc, dpc) from half hc of slot slc; the next unit's products (half hn of
+  // slot sln) are formed into (sn, dpn) interleaved with this unit's elementwise dS, then
+  // dQ^T += K_u^T dS_u^T.  MASK: zero dS where the key is past N or (causal) after the
+  // query; a unit wholly past the wave's last one then adds zeros.
+  auto step = [&](auto MASK, int u, const unsigned char* slc, int hc, const unsigned char* sln, int hn,
+                  f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
+    u32x4 kf = krow(sln, hn, 0), vf = vrow(sln, hn, 0);
     u32x4 pf[2];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      if (k == 0) {
-        sn = zero16();
-        dpn = zero16();
-      }
-      sn = E::mma(kf, qf[k], sn);
-      dpn = E::mma(vf, df[k], dpn);
+      const u32x4 kc = kf, vc = vf;
       if (k + 1 < NS) {
-        kf = krow(kn, k + 1);
-        vf = vrow(vn, k + 1);
+        kf = krow(sln, hn, k + 1);
+        vf = vrow(sln, hn, k + 1);
       }
       dsfrom(sc, dpc, (16 * k) / NS, (16 * (k + 1)) / NS);
+      sn = E::mma(kc, qf[k], k == 0 ? zero16() : sn);
+      dpn = E::mma(vc, df[k], k == 0 ? ndv : dpn);
       if (k == NS - 1) {
+        if constexpr (decltype(MASK)::value) {
+          // keys 32u + 8(v/4) + 4hh + v%4 of this lane's column
+          const int k0 = u * 32;
+          int lim = N - k0 - 4 * hh;
+          if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = 0.f;
+        }
         pf[0] = pack(sc, 0);
         pf[1] = pack(sc, 1);
+        keep(pf[0]);
+        keep(pf[1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    u32x4 tf = ktr(kc, 0, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * NE; ++k) {
-      const int h = k / NE, e = k % NE;
-      const u32x4 cur = tf;
-      if (k + 1 < 2 * NE) tf = ktr(kc, (k + 1) / NE, (k + 1) % NE);
-      acc[e] = E::mma(cur, pf[h], acc[e]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    accumulate(slc, hc, pf);
   };
-
-  // The wave's last unit: diagonal (causal) and/or sequence tail.
-  auto step_last = [&](int u, f32x16& sc, const f32x16& dpc) __attribute__((always_inline)) {
-    const int k0 = u * 32;
-    int lim = N - k0 - 4 * hh;
-    if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
-    dsfrom(sc, dpc, 0, 16);
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = 0.f;
-    const u32x4 pf[2] = {pack(sc, 0), pack(sc, 1)};
-    const int kc = ubase(u, PK);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] = E::mma(ktr(kc, h, e), pf[h], acc[e]);
-  };
-
-  auto step = [&](int u, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
-    if (u < ulast) step_main(u, sc, dpc, sn, dpn);
-    else if (u == ulast) step_last(u, sc, dpc);
-  };
-
-  dma(0);
-  if (ntile > 1) dma(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
   f32x16 sa, pa, sb, pb;
-  {
-    const int k0 = ubase(0, PK), v0 = ubase(0, PV);
-    sa = zero16();
-    pa = zero16();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      sa = E::mma(krow(k0, st), qf[st], sa);
-      pa = E::mma(vrow(v0, st), df[st], pa);
-    }
-  }
-  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
-  const int J1 = min(ntile, ulast0 / 2);
-  auto tile_start = [&](int j) __attribute__((always_inline)) {
+  // Tile j (slot T = j % 3): sync, load tile j+2, units 2j (S, dP in sa, pa) and 2j+1
+  // (in sb, pb).  The products of the unit after the last are formed from a valid slot
+  // and never used.
+  auto tile = [&](auto Tc, auto MASK, int j) __attribute__((always_inline)) {
+    constexpr int T = decltype(Tc)::value;
+    unsigned char* const sc = slot(T);
+    unsigned char* const sn = slot((T + 1) % 3);
     if (j > 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      wait_loads();      // this wave's loads of tile j+1 landed
+      __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
-    if (j + 2 < ntile) dma(j + 2);
+    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    step(MASK, 2 * j, sc, 0, sc, 1, sa, pa, sb, pb);
+    step(MASK, 2 * j + 1, sc, 1, sn, 0, sb, pb, sa, pa);
   };
-  for (int j = 0; j < J1; ++j) {
-    tile_start(j);
-    step_main(2 * j, sa, pa, sb, pb);
-    step_main(2 * j + 1, sb, pb, sa, pa);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using Plain = std::false_type;
+  using Masked = std::true_type;
+
+  dma(0, slot0);
+  if (ntile > 1) dma(1, slot1);
+  wait_loads();
+  __syncthreads();
+  sa = zero16();
+  pa = ndv;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    sa = E::mma(krow(slot0, 0, st), qf[st], sa);
+    pa = E::mma(vrow(slot0, 0, st), df[st], pa);
   }
-  for (int j = J1; j < ntile; ++j) {
-    tile_start(j);
-    step(2 * j, sa, pa, sb, pb);
-    step(2 * j + 1, sb, pb, sa, pa);
+  // Tiles whose units all precede every wave's last unit need no mask.
+  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
+  const int J1 = min(ntile, ulast0 / 2) / 3 * 3;
+  int j = 0;
+  for (; j < J1; j += 3) {
+    tile(I0{}, Plain{}, j);
+    tile(I1{}, Plain{}, j + 1);
+    tile(I2{}, Plain{}, j + 2);
   }
+  for (; j < ntile; j += 3) {
+    tile(I0{}, Masked{}, j);
+    if (j + 1 >= ntile) break;
+    tile(I1{}, Masked{}, j + 1);
+    if (j + 2 >= ntile) break;
+    tile(I2{}, Masked{}, j + 2);
+  }
+  acc_drain(acc);
 
   // dQ = scale * (dQ^T)^T, rounded to the input dtype
   if (myq < N) {
@@ -546,11 +622,11 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.B * a.Hq * a.N;
-  if (rows <= 0) return hipSuccess;
+  const long long prows = (long long)a.B * a.Hq * ((a.N + 31) / 32) * 32;   // padded rows
+  if (prows <= 0) return hipSuccess;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_rowterm_kernel<Tag, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, a, rows);
+  hipLaunchKernelGGL((bwd_rowterm_kernel<Tag, D>), dim3((unsigned)((prows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, a, prows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // d = 128: Q, dO, the dQ accumulator and two units of S, dP need more than the 256

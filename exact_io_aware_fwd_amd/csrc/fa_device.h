@@ -61,6 +61,63 @@ template <> struct Elt<f16_tag> {
   }
 };
 
+// MFMA accumulation into an accumulator held in AGPRs for its whole life (inline asm:
+// the "a" constraint keeps the compiler from moving it between register files).  The
+// compiler does not see these MFMAs, so their hazards are covered by hand:
+//   - VALU write of a B operand -> MFMA read needs 2 wait states: mma_acc_fresh
+//     issues s_nop 1 first; use it for the first MFMA after packing an operand;
+//   - accumulator init (VALU) -> first MFMA: acc_init ends with s_nop 1;
+//   - MFMA write -> VALU read of the accumulator: acc_drain waits 32 cycles.
+// Back-to-back MFMAs on the same accumulator need no wait states (hardware forwarding),
+// and LDS loads feeding the A operand are covered by the compiler's s_waitcnt.
+template <class Tag> struct AccMma;
+template <> struct AccMma<bf16_tag> {
+  static __device__ __forceinline__ void mma(f32x16& acc, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#endif
+  }
+  static __device__ __forceinline__ void mma_fresh(f32x16& acc, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#endif
+  }
+};
+template <> struct AccMma<f16_tag> {
+  static __device__ __forceinline__ void mma(f32x16& acc, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#endif
+  }
+  static __device__ __forceinline__ void mma_fresh(f32x16& acc, u32x4 a, u32x4 b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+#endif
+  }
+};
+template <int N>
+static __device__ __forceinline__ void acc_init(f32x16 (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+a"(acc[i]));
+#endif
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 1");
+#endif
+}
+template <int N>
+static __device__ __forceinline__ void acc_drain(f32x16 (&acc)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 15\n\ts_nop 15");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+#endif
+}
+
 static __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -91,6 +148,12 @@ static __device__ __forceinline__ float half_sum(float x) {
 }
 
 static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt vmcnt(0): this wave's global and buffer loads (LDS DMA included) are done.
+// A workgroup barrier does not wait for them by itself; put this before the barrier
+// that publishes a tile loaded by several waves.  (The builtin, unlike inline asm, is
+// seen by the compiler's wait-count bookkeeping.)
+static __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Compiler fences on values (device pass only; the host pass never sees VGPR constraints).
 // opaque(x): x is redefined here, so nothing computed from it is hoisted above this point.

@@ -28,7 +28,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* rowterm;  // workspace: (LSE_i * log2 e, D_i = sum_k dO_ik O_ik) pairs, [B, Hq, N] fp32x2
+  float* rowterm;  // workspace: per (b, hq) and 32-row block, 32 x LSE_i * log2 e then 32 x -D_i (fp32)
   int B, Hq, Hkv, N;
   float scale;
   float scale_log2;
@@ -38,9 +38,10 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 
-// Workspace of the backward pass: the fp32 row-term pairs, rounded up to 256 bytes.
+// Workspace of the backward pass: two fp32 row terms per query row, rows padded to a
+// multiple of 32 per head (256 bytes per 32-row block).
 inline size_t bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
-  return (size_t)((B * Hq * N * 8 + 255) / 256 * 256);
+  return (size_t)(B * Hq * ((N + 31) / 32) * 256);
 }
 
 }  // namespace fa

@@ -71,9 +71,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  struct ihipStream_t* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: per query row the fp32
- * pair (LSE_i * log2(e), D_i = sum_k dO_ik O_ik), i.e. 8 * B * Hq * N bytes,
- * rounded up to 256.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for these sizes: two fp32 terms per query
+ * row, LSE_i * log2(e) and -D_i with D_i = sum_k dO_ik O_ik, rows padded to a multiple
+ * of 32 per head, i.e. 8 * B * Hq * 32 * ceil(N / 32) bytes.  Returns 0 for invalid
+ * sizes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                              fa_dtype dtype, int causal);
