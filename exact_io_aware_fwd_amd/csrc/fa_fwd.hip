@@ -22,8 +22,9 @@
 //    key order inside each 16-key MFMA step is permuted consistently on both
 //    operands, which the sum over keys does not see.
 //  * Q stays in VGPRs for the whole key loop.  K and V tiles of 64 keys go from
-//    HBM straight into LDS (global_load_lds, 16 bytes per lane, three slots, two
-//    tiles in flight).  Rows are padded to a pitch of row+16 bytes for K and
+//    HBM straight into LDS (buffer loads to LDS, 16 bytes per lane, three slots
+//    that are distinct LDS objects indexed at compile time, two tiles in flight).
+//    Rows are padded to a pitch of row+16 bytes for K and
 //    row+64 bytes for V: with the 64 four-byte banks of the CDNA4 LDS, 16 lanes
 //    reading 16 bytes from 16 consecutive K rows, and 32 lanes reading 8 bytes
 //    from 4 consecutive V rows (ds_read_b64_tr_b16), then hit distinct banks
@@ -35,12 +36,14 @@
 //  * Scores are kept in log2 units.  The reference max is raised only when a
 //    row's max exceeds it by more than 8 (so P <= 256), and O is rescaled only
 //    when some lane of the wave raised it.
-//  * Causal: a workgroup stops at the last tile its rows can see; each wave stops
-//    computing after the tile holding its diagonal, the only tile it masks
-//    (besides the sequence tail).
+//  * Causal: a workgroup stops at the last tile its rows can see.  Tiles before every
+//    wave's diagonal run unmasked; the few after run a masked variant in which a wave
+//    past its diagonal adds only zeros (no branches, so no register shuffling).
 //  * Block ids are remapped so that all query blocks sharing a K/V head run on
 //    one XCD (block ids are dealt round-robin over the 8 XCDs) and the longest
 //    causal blocks start first.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tiles.h"
@@ -65,7 +68,15 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   constexpr int NS = D / 16;            // k-steps of S^T
   constexpr float TAU = 8.f;            // rescale threshold (log2 units)
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * SLOT];
+  // Three slots as distinct LDS objects: tile j uses slot j % 3, known at compile time
+  // in the 3-tile unrolled loops, so the compiler can tell that the loads into one slot
+  // leave the others alone and does not make their reads wait for those loads.
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -99,10 +110,12 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   const int nkv = (N + BC - 1) / BC;
   const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
 
-  // ---- HBM -> LDS: tile t of K and V into slot t % 3 ----
+  // ---- HBM -> LDS: tile t of K and V into slot sl ----
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  auto dma = [&](int t) __attribute__((always_inline)) { Tiles::load(Kg, Vg, N, t, wave, doff, lds + (t % 3) * SLOT); };
+  auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
+    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+  };
 
   // ---- per-lane LDS offsets (plus immediates) ----
   // K (A operand of S^T): row 32c + r32, chunk 2st + hh
@@ -119,31 +132,15 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[e][v] = 0.f;
 
-  // The pipeline works on 32-key units: unit u is half (u & 1) of tile u >> 1.
-  // LDS byte offsets of unit u's K rows / V rows for this lane, kept opaque so that
-  // every read below is "one register + immediate".
-  auto kbase = [&](int u) __attribute__((always_inline)) {
-    int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PK + ka;
-    opaque(r);
-    return r;
+  // The pipeline works on 32-key units: unit 2j + h is half h of tile j.
+  auto kread = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
   };
-  auto vbase = [&](int u) __attribute__((always_inline)) {
-    int r = ((u >> 1) % 3) * SLOT + (u & 1) * 32 * PV + va;
-    opaque(r);
-    return r;
-  };
-  auto kread = [&](int kb, int st) __attribute__((always_inline)) { return *(const u32x4*)(lds + kb + 32 * st); };
-  auto vread = [&](int vb, int h, int e) __attribute__((always_inline)) {
-    return cat(lds_read_tr(lds + vb + 16 * h * PV + 64 * e), lds_read_tr(lds + vb + (16 * h + 8) * PV + 64 * e));
+  auto vread = [&](const unsigned char* sl, int hv, int h, int e) __attribute__((always_inline)) {
+    const unsigned char* p = sl + hv * 32 * PV + va;
+    return cat(lds_read_tr(p + 16 * h * PV + 64 * e), lds_read_tr(p + (16 * h + 8) * PV + 64 * e));
   };
 
-  // Softmax pieces on the scores s of one unit (in log2 units after * c2).
-  auto rowmax = [&](const f32x16& s) __attribute__((always_inline)) {
-    float mx = s[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    return mx;
-  };
   // new reference from the unit's row max; returns alpha = exp2(old - new), sets mref
   auto newref = [&](float mx, bool& raise, float& mref) __attribute__((always_inline)) {
     mx *= c2;
@@ -165,19 +162,25 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
       for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
   };
 
-  // last unit this wave computes: the one holding its diagonal (causal) or the last
-  // holding a key of the sequence
-  const int ulast = (CAUSAL ? min(qw + 31, N - 1) : N - 1) / 32;
-
   // K fragments of the next unit's first two k-steps, read ahead
   u32x4 kpre0, kpre1;
 
-  // Unit u (u < ulast), hand-scheduled.  S-phase: NS slots, each one MFMA of S_{u+1}
-  // plus a share of the softmax of unit u; PV-phase: 2*NE slots, each one MFMA of
-  // O^T += V^T P plus two adds of the row sum.  LDS reads run two slots ahead.
-  auto step_main = [&](int u, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-    const int kb = kbase(u + 1);
-    const int vb = vbase(u);
+  // Unit u (scores in sc; V in half hc of slot slc), hand-scheduled.  S-phase: NS slots,
+  // each one MFMA of S_{u+1} (K in half hn of slot sln) plus a share of the softmax of
+  // unit u; PV-phase: 2*NE slots, each one MFMA of O^T += V^T P plus two adds of the row
+  // sum.  LDS reads run two slots ahead; the last two read unit u+2's first K fragments
+  // (half hp of slot slp).  MASK: scores of keys past N or (causal) after the query are
+  // set to -inf first; a unit wholly past the wave's last one then changes nothing.
+  auto step = [&](auto MASK, int u, const unsigned char* slc, int hc, const unsigned char* sln, int hn,
+                  const unsigned char* slp, int hp, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
+    if constexpr (decltype(MASK)::value) {
+      const int k0 = u * 32;
+      int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
+      if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = -INFINITY;
+    }
     u32x4 kf[NS];
     kf[0] = kpre0;
     kf[1] = kpre1;
@@ -189,8 +192,8 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     for (int k = 0; k < NS; ++k) {
       if (k == 0) sn = zero16();
       sn = E::mma(kf[k], qf[k], sn);
-      if (k + 2 < NS) kf[k + 2] = kread(kb, k + 2);
-      if (k + 2 >= NS) vf[k + 2 - NS] = vread(vb, (k + 2 - NS) / NE, (k + 2 - NS) % NE);
+      if (k + 2 < NS) kf[k + 2] = kread(sln, hn, k + 2);
+      if (k + 2 >= NS) vf[k + 2 - NS] = vread(slc, hc, (k + 2 - NS) / NE, (k + 2 - NS) % NE);
       if (k == 0) {
         mx0 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
 #pragma unroll
@@ -232,84 +235,66 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     for (int k = 0; k < 2 * NE; ++k) {
       const int h = k / NE, e = k % NE;
       o[e] = E::mma(vf[k], pf[h], o[e]);
-      if (k + 2 < 2 * NE) vf[k + 2] = vread(vb, (k + 2) / NE, (k + 2) % NE);
-      if (k == 2 * NE - 2) kpre0 = kread(kbase(u + 2), 0);
-      if (k == 2 * NE - 1) kpre1 = kread(kbase(u + 2), 1);
-      rs += sc[2 * k % 16] + sc[(2 * k + 1) % 16];
-      if (k == 2 * NE - 1 && 4 * NE < 16) {
+      if (k + 2 < 2 * NE) vf[k + 2] = vread(slc, hc, (k + 2) / NE, (k + 2) % NE);
+      if (k == 2 * NE - 2) kpre0 = kread(slp, hp, 0);
+      if (k == 2 * NE - 1) kpre1 = kread(slp, hp, 1);
+      // row sum of the fp32 P (the saved LSE needs it to fp32 accuracy), in this slot
 #pragma unroll
-        for (int v = 4 * NE; v < 16; ++v) rs += sc[v];
-      }
+      for (int v = (16 * k) / (2 * NE); v < (16 * (k + 1)) / (2 * NE); ++v) rs += sc[v];
+      keep(rs);
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run = fmaf(l_run, alpha, rs);
-  };
-
-  // The wave's last unit: diagonal (causal) and/or sequence tail; no next unit.
-  auto step_last = [&](int u, f32x16& sc) __attribute__((always_inline)) {
-    const int k0 = u * 32;
-    int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
-    if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = -INFINITY;
-    bool raise;
-    float mref;
-    const float alpha = newref(half_max(rowmax(sc)), raise, mref);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) rescale(alpha);
-    const u32x4 pf[2] = {packp(sc, 0), packp(sc, 1)};
-    const int vb = vbase(u);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < NE; ++e) o[e] = E::mma(vread(vb, h, e), pf[h], o[e]);
-    float rs = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) rs += sc[v];
-    l_run = fmaf(l_run, alpha, rs);
-  };
-
-  auto step = [&](int u, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-    if (u < ulast) step_main(u, sc, sn);
-    else if (u == ulast) step_last(u, sc);
+    keep(l_run);
   };
 
   // ---- pipeline: two tiles in flight in LDS; S of unit u+1 formed during softmax of u ----
-  dma(0);
-  if (ntile > 1) dma(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
   f32x16 sa, sb;
-  {
-    const int kb = kbase(0);
-    sa = zero16();
-#pragma unroll
-    for (int st = 0; st < NS; ++st) sa = E::mma(kread(kb, st), qf[st], sa);
-    kpre0 = kread(kbase(1), 0);
-    kpre1 = kread(kbase(1), 1);
-  }
-  // Tiles [0, J1): every wave has both units ahead of its last one (branch-free loop).
-  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;   // the smallest ulast
-  const int J1 = min(ntile, ulast0 / 2);
-  auto tile_start = [&](int j) __attribute__((always_inline)) {
+  // Tile j (slot T = j % 3): sync, load tile j+2, units 2j (scores in sa) and 2j+1 (sb).
+  // The products of the unit after the last are formed from a valid slot, never used.
+  auto tile = [&](auto Tc, auto MASK, int j) __attribute__((always_inline)) {
+    constexpr int T = decltype(Tc)::value;
+    unsigned char* const sc = slot(T);
+    unsigned char* const sn = slot((T + 1) % 3);
     if (j > 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile j+1 landed
-      __syncthreads();                                   // everyone's; slot (j-1)%3 is free
+      wait_loads();      // this wave's loads of tile j+1 landed
+      __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
-    if (j + 2 < ntile) dma(j + 2);
+    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    step(MASK, 2 * j, sc, 0, sc, 1, sn, 0, sa, sb);
+    step(MASK, 2 * j + 1, sc, 1, sn, 0, sn, 1, sb, sa);
   };
-  for (int j = 0; j < J1; ++j) {
-    tile_start(j);
-    step_main(2 * j, sa, sb);
-    step_main(2 * j + 1, sb, sa);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using Plain = std::false_type;
+  using Masked = std::true_type;
+
+  dma(0, slot0);
+  if (ntile > 1) dma(1, slot1);
+  wait_loads();
+  __syncthreads();
+  sa = zero16();
+#pragma unroll
+  for (int st = 0; st < NS; ++st) sa = E::mma(kread(slot0, 0, st), qf[st], sa);
+  kpre0 = kread(slot0, 1, 0);
+  kpre1 = kread(slot0, 1, 1);
+  // Tiles whose units all precede every wave's last unit (the one holding its diagonal
+  // when causal, or the last key) need no mask.
+  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
+  const int J1 = min(ntile, ulast0 / 2) / 3 * 3;
+  int j = 0;
+  for (; j < J1; j += 3) {
+    tile(I0{}, Plain{}, j);
+    tile(I1{}, Plain{}, j + 1);
+    tile(I2{}, Plain{}, j + 2);
   }
-  for (int j = J1; j < ntile; ++j) {
-    tile_start(j);
-    step(2 * j, sa, sb);
-    step(2 * j + 1, sb, sa);
+  for (; j < ntile; j += 3) {
+    tile(I0{}, Masked{}, j);
+    if (j + 1 >= ntile) break;
+    tile(I1{}, Masked{}, j + 1);
+    if (j + 2 >= ntile) break;
+    tile(I2{}, Masked{}, j + 2);
   }
 
   // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
