@@ -67,6 +67,8 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   constexpr int NE = D / 32;            // 32-row blocks of O^T
   constexpr int NS = D / 16;            // k-steps of S^T
   constexpr float TAU = 8.f;            // rescale threshold (log2 units)
+  constexpr int PD = 2;                 // LDS read-ahead, in MFMA slots (3 and 4 measured no faster)
+  static_assert(PD <= NS && PD <= 2 * NE, "read-ahead within one phase");
 
   // Three slots as distinct LDS objects: tile j uses slot j % 3, known at compile time
   // in the 3-tile unrolled loops, so the compiler can tell that the loads into one slot
@@ -141,6 +143,12 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     return cat(lds_read_tr(p + 16 * h * PV + 64 * e), lds_read_tr(p + (16 * h + 8) * PV + 64 * e));
   };
 
+  auto rowmax16 = [&](const f32x16& s) __attribute__((always_inline)) {
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    return mx;
+  };
   // new reference from the unit's row max; returns alpha = exp2(old - new), sets mref
   auto newref = [&](float mx, bool& raise, float& mref) __attribute__((always_inline)) {
     mx *= c2;
@@ -163,85 +171,97 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   };
 
   // K fragments of the next unit's first two k-steps, read ahead
-  u32x4 kpre0, kpre1;
+  u32x4 kpre[PD];
 
-  // Unit u (scores in sc; V in half hc of slot slc), hand-scheduled.  S-phase: NS slots,
-  // each one MFMA of S_{u+1} (K in half hn of slot sln) plus a share of the softmax of
-  // unit u; PV-phase: 2*NE slots, each one MFMA of O^T += V^T P plus two adds of the row
-  // sum.  LDS reads run two slots ahead; the last two read unit u+2's first K fragments
-  // (half hp of slot slp).  MASK: scores of keys past N or (causal) after the query are
-  // set to -inf first; a unit wholly past the wave's last one then changes nothing.
-  auto step = [&](auto MASK, int u, const unsigned char* slc, int hc, const unsigned char* sln, int hn,
-                  const unsigned char* slp, int hp, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-    if constexpr (decltype(MASK)::value) {
-      const int k0 = u * 32;
-      int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
-      if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+  // Unit u, hand-scheduled in two phases.
+  // S-phase (scores of unit u in sc, its reference max already chosen): NS slots, each
+  // one MFMA of S_{u+1} (K in half hn of slot sln) plus two of unit u's exponentials;
+  // ends with P packed and O rescaled if unit u raised the reference.
+  // PV-phase (V in half hc of slot slc): 2*NE slots, each one MFMA of O^T += V^T P plus
+  // two adds of the row sum, and the row max of S_{u+1} (masked first under MASK: keys
+  // past N or, causal, after the query), which picks unit u+1's reference; its last PD
+  // slots read unit u+2's first K fragments (half hp of slot slp).
+  // LDS reads run PD slots ahead.
+  struct Ref {
+    float mref;    // reference max (log2 units) the exponentials subtract
+    float alpha;   // exp2(previous reference - mref)
+    bool raise;    // this lane raised the reference
+  };
+  struct Pend {
+    u32x4 pf[2];   // P of the unit, packed B operands of the two 16-key steps
+    u32x4 vpre[PD];  // first PD V fragments of the PV-phase
+  };
+  auto mask_unit = [&](int u, f32x16& s) __attribute__((always_inline)) {
+    const int k0 = u * 32;
+    int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
+    if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = -INFINITY;
-    }
+    for (int v = 0; v < 16; ++v)
+      if (8 * (v >> 2) + (v & 3) >= lim) s[v] = -INFINITY;
+  };
+  auto sphase = [&](const unsigned char* slc, int hc, const unsigned char* sln, int hn, f32x16& sc,
+                    f32x16& sn, const Ref& rf, Pend& pd) __attribute__((always_inline)) {
     u32x4 kf[NS];
-    kf[0] = kpre0;
-    kf[1] = kpre1;
-    float mx0 = 0.f, mx = 0.f, alpha = 1.f, mref = 0.f;
-    bool raise = false;
-    u32x4 vf[2 * NE];
-    u32x4 pf[2];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) kf[i] = kpre[i];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       if (k == 0) sn = zero16();
       sn = E::mma(kf[k], qf[k], sn);
-      if (k + 2 < NS) kf[k + 2] = kread(sln, hn, k + 2);
-      if (k + 2 >= NS) vf[k + 2 - NS] = vread(slc, hc, (k + 2 - NS) / NE, (k + 2 - NS) % NE);
-      if (k == 0) {
-        mx0 = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (k + PD < NS) kf[k + PD] = kread(sln, hn, k + PD);
+      else pd.vpre[k + PD - NS] = vread(slc, hc, (k + PD - NS) / NE, (k + PD - NS) % NE);
 #pragma unroll
-        for (int v = 4; v < 8; ++v) mx0 = fmaxf(mx0, sc[v]);
-      }
-      if (k == 1) {
-        mx = mx0;
-#pragma unroll
-        for (int v = 8; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-        mx = half_max(mx);
-        alpha = newref(mx, raise, mref);
-      }
-      if (k >= 2 && k < NS - 1) {
-        // exps spread over slots 2 .. NS-2
-        constexpr int nslot = NS - 3 > 0 ? NS - 3 : 1;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (2 + (v * nslot) / 16 == k) {
-            sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
-            keep(sc[v]);   // stays in this slot (no sinking past the rescale branch)
-          }
+      for (int v = (16 * k) / NS; v < (16 * (k + 1)) / NS; ++v) {
+        sc[v] = fast_exp2(fmaf(sc[v], c2, -rf.mref));
+        keep(sc[v]);   // stays in this slot (no sinking past the rescale branch)
       }
       if (k == NS - 1) {
-        if (NS <= 3) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sc[v] = fast_exp2(fmaf(sc[v], c2, -mref));
-        }
-        pf[0] = packp(sc, 0);
-        pf[1] = packp(sc, 1);
-        keep(pf[0]);
-        keep(pf[1]);
+        pd.pf[0] = packp(sc, 0);
+        pd.pf[1] = packp(sc, 1);
+        keep(pd.pf[0]);
+        keep(pd.pf[1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) rescale(alpha);
+    if (__builtin_amdgcn_ballot_w64(rf.raise) != 0) rescale(rf.alpha);
     __builtin_amdgcn_sched_barrier(0);
-    float rs = 0.f;
+  };
+  auto pphase = [&](auto MASK, int u, const unsigned char* slc, int hc, const unsigned char* slp, int hp,
+                    const f32x16& sc, f32x16& sn, Ref& rf, const Pend& pd) __attribute__((always_inline)) {
+    u32x4 vf[2 * NE];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) vf[i] = pd.vpre[i];
+    float rs = 0.f, mx = 0.f;
+    const float alpha = rf.alpha;
 #pragma unroll
     for (int k = 0; k < 2 * NE; ++k) {
       const int h = k / NE, e = k % NE;
-      o[e] = E::mma(vf[k], pf[h], o[e]);
-      if (k + 2 < 2 * NE) vf[k + 2] = vread(slc, hc, (k + 2) / NE, (k + 2) % NE);
-      if (k == 2 * NE - 2) kpre0 = kread(slp, hp, 0);
-      if (k == 2 * NE - 1) kpre1 = kread(slp, hp, 1);
+      o[e] = E::mma(vf[k], pd.pf[h], o[e]);
+      if (k + PD < 2 * NE) vf[k + PD] = vread(slc, hc, (k + PD) / NE, (k + PD) % NE);
+      else kpre[k + PD - 2 * NE] = kread(slp, hp, k + PD - 2 * NE);
       // row sum of the fp32 P (the saved LSE needs it to fp32 accuracy), in this slot
 #pragma unroll
       for (int v = (16 * k) / (2 * NE); v < (16 * (k + 1)) / (2 * NE); ++v) rs += sc[v];
       keep(rs);
+      // row max of the next unit's scores (their last MFMA was the S-phase's last slot)
+      if (k == 1) {
+        if constexpr (decltype(MASK)::value) mask_unit(u + 1, sn);
+        mx = fmaxf(fmaxf(sn[0], sn[1]), fmaxf(sn[2], sn[3]));
+#pragma unroll
+        for (int v = 4; v < 8; ++v) mx = fmaxf(mx, sn[v]);
+        keep(mx);
+      }
+      if (k == 2) {
+#pragma unroll
+        for (int v = 8; v < 16; ++v) mx = fmaxf(mx, sn[v]);
+        mx = half_max(mx);
+        keep(mx);
+      }
+      if (k == 3) {
+        rf.alpha = newref(mx, rf.raise, rf.mref);
+        keep(rf.alpha);
+        keep(rf.mref);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run = fmaf(l_run, alpha, rs);
@@ -249,20 +269,33 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   };
 
   // ---- pipeline: two tiles in flight in LDS; S of unit u+1 formed during softmax of u ----
+  // The two waves that share a SIMD (w and w + 4) run half a unit apart: the second
+  // group (LATE) passes each tile barrier after, not before, the S-phase of the tile's
+  // first unit, so one wave's softmax runs while the other's PV products keep the
+  // matrix core busy (the FA3 section's ping-pong between warpgroups, on one SIMD).
+  // With three slots this is safe: nothing reads tile j-1 after barrier j, and the
+  // early S-phase reads only tile j, published at barrier j-1.
   f32x16 sa, sb;
+  Ref rf;
   // Tile j (slot T = j % 3): sync, load tile j+2, units 2j (scores in sa) and 2j+1 (sb).
-  // The products of the unit after the last are formed from a valid slot, never used.
-  auto tile = [&](auto Tc, auto MASK, int j) __attribute__((always_inline)) {
+  // MASK masks the units after this tile's first (the first was masked, if needed, by
+  // the phase before it).  The products of the unit after the last are formed from a
+  // valid slot and never used (masked: the last tile always runs masked).
+  auto tile = [&](auto Tc, auto MASK, auto LATE, int j) __attribute__((always_inline)) {
     constexpr int T = decltype(Tc)::value;
     unsigned char* const sc = slot(T);
     unsigned char* const sn = slot((T + 1) % 3);
+    Pend p0, p1;
+    if constexpr (decltype(LATE)::value) sphase(sc, 0, sc, 1, sa, sb, rf, p0);
     if (j > 0) {
       wait_loads();      // this wave's loads of tile j+1 landed
       __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
     if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
-    step(MASK, 2 * j, sc, 0, sc, 1, sn, 0, sa, sb);
-    step(MASK, 2 * j + 1, sc, 1, sn, 0, sn, 1, sb, sa);
+    if constexpr (!decltype(LATE)::value) sphase(sc, 0, sc, 1, sa, sb, rf, p0);
+    pphase(MASK, 2 * j, sc, 0, sn, 0, sa, sb, rf, p0);
+    sphase(sc, 1, sn, 0, sb, sa, rf, p1);
+    pphase(MASK, 2 * j + 1, sc, 1, sn, 1, sb, sa, rf, p1);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -277,25 +310,31 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   sa = zero16();
 #pragma unroll
   for (int st = 0; st < NS; ++st) sa = E::mma(kread(slot0, 0, st), qf[st], sa);
-  kpre0 = kread(slot0, 1, 0);
-  kpre1 = kread(slot0, 1, 1);
-  // Tiles whose units all precede every wave's last unit (the one holding its diagonal
-  // when causal, or the last key) need no mask.
+#pragma unroll
+  for (int i = 0; i < PD; ++i) kpre[i] = kread(slot0, 1, i);
+  mask_unit(0, sa);
+  rf.alpha = newref(half_max(rowmax16(sa)), rf.raise, rf.mref);
+  // Tiles whose units, and the unit after them, all precede every wave's last unit (the
+  // one holding its diagonal when causal, or the last key) need no mask.
   const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
-  const int J1 = min(ntile, ulast0 / 2) / 3 * 3;
-  int j = 0;
-  for (; j < J1; j += 3) {
-    tile(I0{}, Plain{}, j);
-    tile(I1{}, Plain{}, j + 1);
-    tile(I2{}, Plain{}, j + 2);
-  }
-  for (; j < ntile; j += 3) {
-    tile(I0{}, Masked{}, j);
-    if (j + 1 >= ntile) break;
-    tile(I1{}, Masked{}, j + 1);
-    if (j + 2 >= ntile) break;
-    tile(I2{}, Masked{}, j + 2);
-  }
+  const int J1 = min(ntile, max(ulast0 - 1, 0) / 2) / 3 * 3;
+  auto run = [&](auto LATE) __attribute__((always_inline)) {
+    int j = 0;
+    for (; j < J1; j += 3) {
+      tile(I0{}, Plain{}, LATE, j);
+      tile(I1{}, Plain{}, LATE, j + 1);
+      tile(I2{}, Plain{}, LATE, j + 2);
+    }
+    for (; j < ntile; j += 3) {
+      tile(I0{}, Masked{}, LATE, j);
+      if (j + 1 >= ntile) break;
+      tile(I1{}, Masked{}, LATE, j + 1);
+      if (j + 2 >= ntile) break;
+      tile(I2{}, Masked{}, LATE, j + 2);
+    }
+  };
+  if (wave >= NW / 2) run(std::true_type{});
+  else run(std::false_type{});
 
   // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
   const float l_tot = half_sum(l_run);
