@@ -6,7 +6,9 @@ CPU-baseline leg of ``bench.py`` use it.  It shares no code with the HIP path.
 
 It is the plain, materialising definition of scaled dot-product attention written
 out in numpy float64 (see :mod:`oracle.attention` for the passages each function
-follows), plus the footprint arithmetic of the pages' worked example.
+follows), plus the footprint arithmetic of the pages' worked example, and the
+few-queries / long-key-sequence case with the log-sum-exp combine of split-KV
+decoding (:mod:`oracle.decode`).
 """
 from .attention import (
     attention_fwd,
@@ -15,6 +17,7 @@ from .attention import (
     materialised_bytes,
     to_f64,
 )
+from .decode import attention_fwd_kv, lse_combine
 
 __all__ = [
     "attention_fwd",
@@ -22,4 +25,6 @@ __all__ = [
     "attention_probs",
     "materialised_bytes",
     "to_f64",
+    "attention_fwd_kv",
+    "lse_combine",
 ]
