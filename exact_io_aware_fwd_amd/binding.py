@@ -50,6 +50,15 @@ def load() -> ctypes.CDLL:
     L.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                          _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_float, _i64, _vp]
+    L.fa_fwd_splitkv.restype = ctypes.c_int
+    L.fa_fwd_splitkv_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _i64]
+    L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    L.fa_fwd_splitkv_num_splits.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64]
+    L.fa_fwd_splitkv_num_splits.restype = _i64
+    L.fa_lse_combine.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
+    L.fa_lse_combine.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -61,7 +70,7 @@ def load() -> ctypes.CDLL:
 def declared_symbols() -> list[str]:
     """Names of the functions include/fa.h declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, re.M)))
 
 
 def status_string(status: int) -> str:
@@ -164,3 +173,68 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
     if st != FA_OK:
         _raise(st)
     return dq, dk, dv
+
+
+def splitkv_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype, num_splits: int = 0) -> int:
+    code = FA_BF16 if dtype == torch.bfloat16 else FA_F16
+    return int(load().fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, code, num_splits))
+
+
+def splitkv_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, softmax_scale: float | None = None, num_splits: int = 0,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None):
+    """O, LSE of q [B,Hq,Nq,d] against k/v [B,Hkv,Nk,d] via fa_fwd_splitkv (split-KV decoding).
+
+    Query i is at position Nk - Nq + i (causal: sees keys j <= Nk - Nq + i).
+    """
+    L = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, Hkv, Nk, d] matching q {tuple(q.shape)}; got {tuple(k.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dev, q.dtype)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(o, "out", dev, q.dtype)
+    _check(lse_t, "lse", dev, torch.float32)
+    need = splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, q.dtype, num_splits)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _check(ws, "workspace", dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                              ws.data_ptr(), ws.numel(), B, Hq, Hkv, Nq, Nk, d, _dtype_code(q),
+                              int(bool(causal)), scale, int(num_splits), stream)
+    if st != FA_OK:
+        _raise(st)
+    return o, lse_t
+
+
+def lse_combine(o_parts: torch.Tensor, lse_parts: torch.Tensor, dtype=torch.bfloat16):
+    """Merge partial results: o_parts [rows, S, d] fp32, lse_parts [rows, S] fp32 -> (O [rows, d], LSE [rows])."""
+    L = load()
+    if o_parts.dim() != 3 or lse_parts.dim() != 2 or o_parts.shape[:2] != lse_parts.shape:
+        raise ValueError("o_parts must be [rows, S, d] and lse_parts [rows, S]")
+    rows, S, d = o_parts.shape
+    dev = o_parts.device
+    _check(o_parts, "o_parts", dev, torch.float32)
+    _check(lse_parts, "lse_parts", dev, torch.float32)
+    o = torch.empty((rows, d), dtype=dtype, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    code = FA_BF16 if dtype == torch.bfloat16 else FA_F16
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_lse_combine(o_parts.data_ptr(), lse_parts.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              rows, S, d, code, stream)
+    if st != FA_OK:
+        _raise(st)
+    return o, lse

@@ -66,6 +66,40 @@ fa_status check_ptr(const void* p, const char* name) {
 
 }  // namespace
 
+namespace {
+
+// Size checks of the split-KV forward.  Sets *empty when there is nothing to compute.
+fa_status check_splitkv_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                              fa_dtype dtype, int causal, int64_t num_splits, bool* empty) {
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B, Nq and Nk must be >= 0 (B=%lld Nq=%lld Nk=%lld)", (long long)B,
+                (long long)Nq, (long long)Nk);
+  if (Hq < 1 || Hkv < 1) return fail(FA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be >= 1 (Hq=%lld Hkv=%lld)",
+                                     (long long)Hq, (long long)Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                                 (long long)Hq, (long long)Hkv);
+  if (d < 1) return fail(FA_ERR_INVALID_ARGUMENT, "d must be >= 1 (d=%lld)", (long long)d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                                       (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be >= 0 (got %lld)", (long long)num_splits);
+  // per-head K/V byte offsets are 32-bit in the kernel; rows and splits are 32-bit
+  if (B > INT_MAX || Hq > INT_MAX || Nq > INT_MAX || Nk > INT_MAX / 2 || Nk * d > INT_MAX / 2 ||
+      B * Hq > INT_MAX || B * Hq * Nq > INT_MAX || num_splits > INT_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes exceed the supported index range");
+  *empty = (B == 0 || Nq == 0);
+  if (*empty) return FA_OK;
+  if (Nk == 0) return fail(FA_ERR_INVALID_ARGUMENT, "Nk = 0: the queries have no keys");
+  if (causal && Nq > Nk)
+    return fail(FA_ERR_INVALID_ARGUMENT, "causal needs Nq <= Nk (Nq=%lld Nk=%lld)", (long long)Nq, (long long)Nk);
+  const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits);
+  if ((int64_t)B * Hkv * p.RG * (p.S4 / 4) > (int64_t)UINT_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fa_status_string(fa_status s) {
@@ -159,6 +193,85 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.scale_log2 = softmax_scale * kLog2e;
   const hipError_t err = fa::launch_bwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                     fa_dtype dtype, int64_t num_splits) {
+  bool empty = false;
+  if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, dtype, 0, num_splits, &empty) != FA_OK) return 0;
+  if (empty) return 0;
+  return fa::splitkv_workspace_bytes(B, Hq, Nq, d, fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits));
+}
+
+int64_t fa_fwd_splitkv_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  bool empty = false;
+  if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, FA_BF16, 0, 0, &empty) != FA_OK || empty) return 0;
+  const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, 0);
+  return (Nk + p.C - 1) / p.C;
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                         int64_t d, fa_dtype dtype, int causal, float softmax_scale, int64_t num_splits,
+                         struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, dtype, causal, num_splits, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(k, "k")) != FA_OK ||
+      (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
+      (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
+    return st;
+  const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits);
+  const size_t need = fa::splitkv_workspace_bytes(B, Hq, Nq, d, p);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.opart = static_cast<float*>(workspace);
+  a.lpart = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + fa::splitkv_opart_bytes(B, Hq, Nq, d, p));
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Nq = (int)Nq;
+  a.Nk = (int)Nk;
+  a.RG = p.RG;
+  a.C = p.C;
+  a.S4 = p.S4;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t err = fa::launch_splitkv(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "split-KV launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, float* lse, int64_t rows,
+                         int64_t num_parts, int64_t d, fa_dtype dtype, struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  if (rows < 0) return fail(FA_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (num_parts < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_parts must be >= 1 (got %lld)", (long long)num_parts);
+  if (d < 1) return fail(FA_ERR_INVALID_ARGUMENT, "d must be >= 1 (d=%lld)", (long long)d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                                       (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (num_parts > INT_MAX || rows > (int64_t)INT_MAX * 65536)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes exceed the supported index range");
+  if (rows == 0) return FA_OK;
+  fa_status st;
+  if ((st = check_ptr(o_parts, "o_parts")) != FA_OK || (st = check_ptr(lse_parts, "lse_parts")) != FA_OK ||
+      (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK)
+    return st;
+  const hipError_t err = fa::launch_lse_combine(o_parts, lse_parts, o, lse, (long long)rows, (int)num_parts, (int)d,
+                                                dtype == FA_BF16, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(err));
   return FA_OK;
 }
 

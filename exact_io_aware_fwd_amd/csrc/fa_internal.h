@@ -34,9 +34,59 @@ struct BwdArgs {
   float scale_log2;
 };
 
+// Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* opart;    // workspace: partial O per (row, split), [B*Hq*Nq, S4, d] fp32
+  float* lpart;    // workspace: partial LSE per (row, split), [B*Hq*Nq, S4] fp32 (natural log)
+  int B, Hq, Hkv, Nq, Nk;
+  int RG;          // 32-row groups per (batch, K/V head): ceil(Hq/Hkv * Nq / 32)
+  int C;           // keys per split (a multiple of 32)
+  int S4;          // splits, padded to a multiple of 4 (one wave each)
+  float scale;
+  float scale_log2;
+};
+
+// How the keys are split.  num_splits = 0 picks a count that gives about four waves
+// per CU in one round (1024 waves on 256 CUs).
+struct SplitPlan {
+  int RG, C, S4;
+};
+inline SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t num_splits) {
+  SplitPlan p;
+  const int64_t G = Hq / Hkv;
+  p.RG = (int)((G * Nq + 31) / 32);
+  const int64_t units = (Nk + 31) / 32;
+  int64_t S = num_splits;
+  if (S <= 0) {
+    const int64_t groups = B * Hkv * p.RG;
+    S = (1024 + groups - 1) / groups;
+  }
+  if (S > units) S = units;
+  if (S < 1) S = 1;
+  const int64_t per = (units + S - 1) / S;             // units per split
+  p.C = (int)(per * 32);
+  const int64_t used = (Nk + p.C - 1) / p.C;           // non-empty splits
+  p.S4 = (int)((used + 3) / 4 * 4);
+  return p;
+}
+inline size_t splitkv_opart_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, const SplitPlan& p) {
+  return (size_t)((B * Hq * Nq * p.S4 * d * 4 + 255) / 256 * 256);
+}
+inline size_t splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, const SplitPlan& p) {
+  return splitkv_opart_bytes(B, Hq, Nq, d, p) + (size_t)((B * Hq * Nq * p.S4 * 4 + 255) / 256 * 256);
+}
+
 // Return a hipError_t from the launches (hipSuccess when all were enqueued).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_splitkv(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, float* lse, long long rows, int S,
+                              int d, bool bf16, hipStream_t stream);
 
 // Workspace of the backward pass: two fp32 row terms per query row, rows padded to a
 // multiple of 32 per head (256 bytes per 32-row block).

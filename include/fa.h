@@ -104,6 +104,62 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  fa_dtype dtype, int causal, float softmax_scale,
                  struct ihipStream_t* stream);
 
+/*
+ * Split-KV forward for decoding: Nq new queries against a long key/value sequence.
+ *
+ * Follows "Flash Attention" (wiki), sections "Training and autoregressive decoding"
+ * and "Flash-Decoding": the key/value sequence is cut into splits, each split is
+ * attended with the tiled online-softmax recurrence of fa_fwd, and the partial
+ * outputs are merged with their log-sum-exp statistics (fa_lse_combine's rule).
+ * The result equals exact attention of the queries over all keys (up to rounding).
+ *
+ *   q   [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]   inputs, `dtype`, 16-byte aligned
+ *   o   [B,Hq,Nq,d]                     output, `dtype` (RNE)
+ *   lse [B,Hq,Nq] float32               output: ln sum_j exp(S_ij) (natural log)
+ *   The queries are the last Nq positions of the sequence: query i is at position
+ *   Nk - Nq + i; with `causal` set it sees keys j <= Nk - Nq + i (requires Nq <= Nk).
+ *   num_splits: key splits per (batch, K/V head, 32-row group); 0 picks a default
+ *   (fa_fwd_splitkv_num_splits).  The split size is rounded to 32 keys.
+ *   workspace, workspace_bytes >= fa_fwd_splitkv_workspace_size(... same num_splits),
+ *   16-byte aligned; contents on entry are ignored.
+ *   B = 0 or Nq = 0: nothing to do, FA_OK.  Nk = 0 with Nq > 0 is invalid (no keys).
+ * Same dtype/d rules and status codes as fa_fwd.
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                         fa_dtype dtype, int causal, float softmax_scale, int64_t num_splits,
+                         struct ihipStream_t* stream);
+
+/*
+ * Bytes of workspace fa_fwd_splitkv needs: per output row and split, the fp32 partial
+ * O (d floats) and partial LSE, splits padded to a multiple of 4.  0 for invalid sizes.
+ */
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                     fa_dtype dtype, int64_t num_splits);
+
+/* The number of key splits fa_fwd_splitkv uses for num_splits = 0 (before padding to
+ * a multiple of 4); 0 for invalid sizes. */
+int64_t fa_fwd_splitkv_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d);
+
+/*
+ * Merge partial attention results over disjoint key sets ("Flash Attention" wiki,
+ * section "Flash-Decoding": partial outputs combined by their log-sum-exp
+ * statistics; also the merge step of ring attention).  For each row:
+ *   M = max_s LSE_s,  w_s = exp(LSE_s - M),
+ *   O = sum_s w_s O_s / sum_s w_s,  LSE = M + ln sum_s w_s,
+ * parts with LSE_s = -inf carry no weight; a row whose parts are all -inf gets O = 0
+ * and LSE = -inf.
+ *
+ *   o_parts   [rows, num_parts, d] float32   each O_s normalised over its own keys
+ *   lse_parts [rows, num_parts]    float32   natural log
+ *   o [rows, d] `dtype` (RNE), lse [rows] float32   outputs
+ *   rows >= 0 (0: nothing to do), num_parts >= 1, d in {64, 128}; pointers 16-byte aligned.
+ */
+fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                         int64_t rows, int64_t num_parts, int64_t d, fa_dtype dtype,
+                         struct ihipStream_t* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

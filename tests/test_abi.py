@@ -11,6 +11,7 @@ import math
 import subprocess
 
 import pytest
+import torch
 
 from exact_io_aware_fwd_amd import binding
 
@@ -25,7 +26,9 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = binding.declared_symbols()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
+                          "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_num_splits",
+                          "fa_lse_combine"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -111,3 +114,47 @@ def test_python_binding_validates_before_the_abi():
         binding.fwd(q, q, q)          # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         binding._dtype_code(torch.zeros(1, dtype=torch.float32))
+
+
+def splitkv(L, ws_bytes=1 << 24, B=1, Hq=8, Hkv=2, Nq=1, Nk=100, d=128, dtype=1, causal=0, scale=0.125, S=0,
+            **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "ws")}
+    p.update(ptrs)
+    return L.fa_fwd_splitkv(p["q"], p["k"], p["v"], p["o"], p["lse"], p["ws"], ws_bytes,
+                            B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale, S, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INV), (dict(ws=None), INV), (dict(o=P + 4), INV), (dict(Nk=-1), INV), (dict(Nq=-1), INV),
+    (dict(Hq=3), INV), (dict(Nk=0), INV), (dict(causal=1, Nq=8, Nk=4), INV), (dict(S=-2), INV),
+    (dict(d=96), UNS), (dict(dtype=5), UNS), (dict(scale=0.0), INV), (dict(ws_bytes=64), INV),
+    (dict(Nk=1 << 31), INV),
+])
+def test_splitkv_rejects(L, kw, expect):
+    assert splitkv(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(Nq=0, Nk=0, q=None, ws=None)])
+def test_splitkv_empty_is_noop(L, kw):
+    assert splitkv(L, **kw) == OK
+
+
+def test_splitkv_plan():
+    # default splits: about 1024 waves over (batch, K/V head, 32-row group); each split a
+    # multiple of 32 keys; workspace = rows x splits (padded to 4) x (d + 1) floats
+    assert binding.splitkv_num_splits(1, 64, 8, 1, 65536, 128) == 128
+    assert binding.splitkv_num_splits(2, 32, 8, 4, 8192, 128) == 64
+    assert binding.splitkv_num_splits(1, 8, 2, 1, 40, 64) == 2      # at most one split per 32 keys
+    ws = binding.splitkv_workspace_size(1, 64, 8, 1, 65536, 128, torch.bfloat16)
+    assert ws == 64 * 128 * 128 * 4 + 64 * 128 * 4
+    assert binding.splitkv_workspace_size(1, 8, 2, 1, 40, 64, torch.bfloat16, 3) == 8 * 4 * 64 * 4 + 256
+    assert binding.splitkv_workspace_size(1, 8, 3, 1, 40, 64, torch.bfloat16) == 0
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((P, P, P, P, -1, 2, 128, 1), INV), ((P, P, P, P, 4, 0, 128, 1), INV), ((P, P, P, P, 4, 2, 80, 1), UNS),
+    ((None, P, P, P, 4, 2, 128, 1), INV), ((P, P, P + 2, P, 4, 2, 128, 1), INV), ((P, P, P, P, 0, 2, 128, 1), OK),
+])
+def test_lse_combine_validation(L, args, expect):
+    assert L.fa_lse_combine(*args, None) == expect

@@ -9,7 +9,8 @@ The five workloads are the kernel-level shapes named for this attention path:
 a single-head check, an 8-head d=64 fp16 case with the same shape and dtype as
 the flash-attention-sm75 README's usage example, a bf16 d=128 causal case with
 enlarged queries on half the heads, a grouped-query long-context case, and a
-forward+backward case.
+forward+backward case.  Two decoding shapes (few queries, long key/value
+sequence) serve the split-KV forward.
 """
 from __future__ import annotations
 
@@ -67,6 +68,54 @@ WORKLOADS = {
 
 # The workload the throughput metric is quoted on (N=8192, d=128, bf16, causal).
 HEADLINE = "gqa_b2_hq32_hkv8_n8192_d128_bf16_causal"
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new queries against Nk cached keys/values (split-KV decoding)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: tuple
+    seeds: tuple
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def torch_dtype(self):
+        return {"fp16": torch.float16, "bf16": torch.bfloat16}[self.dtype]
+
+
+# Decoding shapes.  The "Flash Attention" wiki's "Flash-Decoding" section quotes a
+# batch-one, long-context benchmark on a 34B code model; that model's attention
+# layout (64 query heads sharing 8 K/V heads, d = 128: its public configuration, not
+# a number on the pages) with one new token and a 64K cache stands in for it.  The second case is the headline workload's head layout
+# with four new tokens (causal, bottom-right aligned) against an 8K cache.
+DECODE_WORKLOADS = {
+    "decode_b1_hq64_hkv8_nq1_nk65536_d128_bf16": DecodeWorkload(
+        "decode_b1_hq64_hkv8_nq1_nk65536_d128_bf16", 1, 64, 8, 1, 65536, 128, "bf16", (False,), (6000, 6001, 6002),
+        note="one new token against a 64K cache; HBM-bound"),
+    "decode_b2_hq32_hkv8_nq4_nk8192_d128_bf16_causal": DecodeWorkload(
+        "decode_b2_hq32_hkv8_nq4_nk8192_d128_bf16_causal", 2, 32, 8, 4, 8192, 128, "bf16", (True, False),
+        (7000, 7001, 7002), note="four new tokens, causal (bottom-right) and not"),
+}
+DECODE_HEADLINE = "decode_b1_hq64_hkv8_nq1_nk65536_d128_bf16"
+
+
+def make_decode_inputs(w: DecodeWorkload, Nk: int | None = None):
+    """CPU tensors (q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d]) for decode workload `w`."""
+    Nk = w.Nk if Nk is None else Nk
+    dt = w.torch_dtype
+    return (randn(w.seeds[0], (w.B, w.Hq, w.Nq, w.d), dt), randn(w.seeds[1], (w.B, w.Hkv, Nk, w.d), dt),
+            randn(w.seeds[2], (w.B, w.Hkv, Nk, w.d), dt))
 
 
 def randn(seed: int, shape, dtype) -> torch.Tensor:
