@@ -26,8 +26,9 @@
 //  * The three V slots are distinct LDS objects indexed at compile time (the unit
 //    loop is unrolled by 3), so the compiler does not make the transposing reads of
 //    one slot wait for the loads into another.
-//  * Each split writes its normalised partial O (fp32) and partial LSE; the combine
-//    kernel merges them per row.
+//  * The four splits of a workgroup merge their partial results in LDS; the workgroup
+//    writes one normalised partial O (fp32) and partial LSE per row, and the combine
+//    kernel merges those per row.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -113,11 +114,7 @@ __global__ void __launch_bounds__(256) splitkv_kernel(const DecodeArgs a) {
   const int qpos = Nk - Nq + qi;                      // absolute position of the query
   const long long orow = ((long long)(b * a.Hq + hq)) * Nq + qi;
 
-  if (ks >= ke) {                                     // empty split: no keys
-    if (valid && hh == 0) a.lpart[orow * a.S4 + s] = -INFINITY;
-    return;
-  }
-  const int nunit = (ke - ks + 31) / 32;
+  const int nunit = ks < ke ? (ke - ks + 31) / 32 : 0;   // 0: an empty split (past the keys)
 
   // Q^T as the B operand: lane holds Q[row][16st + 8hh .. +7]
   u32x4 qf[NS];
@@ -225,7 +222,7 @@ __global__ void __launch_bounds__(256) splitkv_kernel(const DecodeArgs a) {
   using I2 = std::integral_constant<int, 2>;
 
   u32x4 kA[NS], kB[NS], kC[NS];
-  issue(0, kA, vs0);
+  if (nunit > 0) issue(0, kA, vs0);
   if (nunit > 1) issue(1, kB, vs1);
   for (int u = 0; u < nunit; u += 3) {
     step(I0{}, u, kA, kC);
@@ -235,10 +232,15 @@ __global__ void __launch_bounds__(256) splitkv_kernel(const DecodeArgs a) {
     step(I2{}, u + 2, kC, kB);
   }
 
-  // partial result of this split: O normalised over its keys, LSE in natural log
+  // Partial result of this split (O normalised over its keys, LSE in natural log),
+  // merged in LDS with the other three splits of the workgroup by the combine rule; the
+  // workgroup writes one part per row.  The V slots are reused once every wave is done.
   const float l_tot = half_sum(l_run);
-  if (valid) {
-    float* op = a.opart + (orow * a.S4 + s) * D;
+  const float lse_w = l_tot > 0.f ? (mr + log2f(l_tot)) * kLn2 : -INFINITY;
+  __syncthreads();
+  float* po = (float*)(wave < 2 ? vs0 : vs1) + (wave & 1) * 32 * D;   // [32 rows][D] of this wave
+  float* pl = (float*)vs2 + wave * 32;                               // [32 rows]
+  {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -247,99 +249,122 @@ __global__ void __launch_bounds__(256) splitkv_kernel(const DecodeArgs a) {
         const int d0 = 32 * e + 8 * g4 + 4 * hh;
         const f32x4 w = {o[e][4 * g4 + 0] * inv, o[e][4 * g4 + 1] * inv, o[e][4 * g4 + 2] * inv,
                          o[e][4 * g4 + 3] * inv};
-        *(f32x4*)(op + d0) = w;
+        *(f32x4*)(po + r32 * D + d0) = w;
       }
-    if (hh == 0) a.lpart[orow * a.S4 + s] = l_tot > 0.f ? (mr + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (hh == 0) pl[r32] = lse_w;
+  }
+  __syncthreads();
+  // thread t: row t / 8, elements (t % 8) * D/8 .. +D/8
+  {
+    constexpr int EPT = D / 8;
+    const int t = threadIdx.x, row = t >> 3, e0 = (t & 7) * EPT;
+    const int rr = rg * 32 + row;
+    if (rr < G * Nq) {
+      const int rg_g = rr / Nq, rq = rr - rg_g * Nq;
+      const long long orr = ((long long)(b * a.Hq + hkv * G + rg_g)) * Nq + rq;
+      float lw[NW], M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        lw[w] = ((const float*)vs2)[w * 32 + row];
+        M = fmaxf(M, lw[w]);
+      }
+      float wt[NW], den = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        wt[w] = (M == -INFINITY || lw[w] == -INFINITY) ? 0.f : fast_exp2((lw[w] - M) * kLog2e);
+        den += wt[w];
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      const int P = a.S4 / NW;                        // parts per row: one per workgroup
+      float* dst = a.opart + (orr * P + quad) * D + e0;
+#pragma unroll
+      for (int i = 0; i < EPT; i += 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          if (wt[w] == 0.f) continue;
+          const float* src = (const float*)(w < 2 ? vs0 : vs1) + (w & 1) * 32 * D + row * D + e0 + i;
+          const f32x4 x = *(const f32x4*)src;
+          acc += wt[w] * x;
+        }
+        *(f32x4*)(dst + i) = acc * inv;
+      }
+      if ((t & 7) == 0) a.lpart[orr * P + quad] = den > 0.f ? M + logf(den) : -INFINITY;
+    }
   }
 }
 
 // ---- combine: per row, O = sum_s w_s O_s / sum_s w_s, LSE = M + ln sum_s w_s,
 // w_s = exp(LSE_s - M), M = max_s LSE_s; parts with LSE_s = -inf carry no weight.
-// One 256-thread workgroup per row: the statistics are reduced across the workgroup,
-// the weights kept in LDS, and 256/D groups of D threads each sum a share of the parts
-// (loads unrolled so that several are in flight), then the groups are added in LDS.
+// One 256-thread workgroup per row: 256/D groups of D threads each take every
+// (256/D)-th part, loading a chunk of parts at once (one memory round trip per chunk)
+// and merging chunks with a running maximum; the groups are merged in LDS.
 template <class Tag, int D>
 __global__ void __launch_bounds__(256) lse_combine_kernel(const float* opart, const float* lpart, void* o, float* lse,
                                                           long long rows, int S) {
   using E = Elt<Tag>;
   constexpr int NT = 256;
   constexpr int NG = NT / D;            // thread groups over the parts
-  constexpr int WCAP = 2048;            // parts whose weights stay in LDS
-  __shared__ float wts[WCAP];
-  __shared__ float red[NT / 64];
-  __shared__ float part[NG][D];
+  constexpr int CH = 16;                // parts per thread per chunk
+  __shared__ float gm[NG], gden[NG];
+  __shared__ float gacc[NG][D];
   const long long row = (long long)blockIdx.y * gridDim.x + blockIdx.x;
   if (row >= rows) return;              // uniform per workgroup
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const float* lp = lpart + row * S;
-  const float* op = opart + row * (long long)S * D;
-
-  float m = -INFINITY;
-  for (int s = t; s < S; s += NT) m = fmaxf(m, lp[s]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if (lane == 0) red[wv] = m;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, red[i]);
-  __syncthreads();
-
-  float dsum = 0.f;
-  for (int s = t; s < S; s += NT) {
-    const float l = lp[s];
-    const float w = (M == -INFINITY || l == -INFINITY) ? 0.f : fast_exp2((l - M) * kLog2e);
-    dsum += w;
-    if (s < WCAP) wts[s] = w;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
-  if (lane == 0) red[wv] = dsum;
-  __syncthreads();
-  float den = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) den += red[i];
-
-  // group g sums parts s = g, g + NG, ... for element e
+  const int t = threadIdx.x;
   const int g = t / D, e = t - (t / D) * D;
-  float acc = 0.f;
-  int s = g;
-  for (; s + 3 * NG < S; s += 4 * NG) {
-    float x[4], w[4];
+  const float* lp = lpart + row * S;
+  const float* op = opart + row * (long long)S * D + e;
+  float m = -INFINITY, den = 0.f, acc = 0.f;
+  for (int base = g; base < S; base += NG * CH) {
+    float lv[CH], ov[CH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int si = s + i * NG;
-      w[i] = si < WCAP ? wts[si] : 0.f;
-      if (si >= WCAP) {
-        const float l = lp[si];
-        w[i] = (M == -INFINITY || l == -INFINITY) ? 0.f : fast_exp2((l - M) * kLog2e);
-      }
-      x[i] = w[i] != 0.f ? op[(long long)si * D + e] : 0.f;
+    for (int i = 0; i < CH; ++i) {
+      const int si = base + i * NG;
+      lv[i] = si < S ? lp[si] : -INFINITY;
+      ov[i] = si < S ? op[(long long)si * D] : 0.f;
     }
+    float cm = lv[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = fmaf(w[i], x[i], acc);
-  }
-  for (; s < S; s += NG) {
-    float w = s < WCAP ? wts[s] : 0.f;
-    if (s >= WCAP) {
-      const float l = lp[s];
-      w = (M == -INFINITY || l == -INFINITY) ? 0.f : fast_exp2((l - M) * kLog2e);
+    for (int i = 1; i < CH; ++i) cm = fmaxf(cm, lv[i]);
+    const float nm = fmaxf(m, cm);
+    if (nm == -INFINITY) continue;
+    const float sc = m == -INFINITY ? 0.f : fast_exp2((m - nm) * kLog2e);
+    den *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (lv[i] == -INFINITY) continue;           // empty part: its O was never written
+      const float w = fast_exp2((lv[i] - nm) * kLog2e);
+      den += w;
+      acc = fmaf(w, ov[i], acc);
     }
-    if (w != 0.f) acc = fmaf(w, op[(long long)s * D + e], acc);
+    m = nm;
   }
-  part[g][e] = acc;
+  if (e == 0) {
+    gm[g] = m;
+    gden[g] = den;
+  }
+  gacc[g][e] = acc;
   __syncthreads();
   if (t < D) {
-    float sum = 0.f;
+    float M = gm[0];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) sum += part[i][t];
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    // pairs of elements packed by the even thread
-    const float nb = __shfl_down(sum, 1, 64);
-    if ((t & 1) == 0)
-      *(uint32_t*)((unsigned char*)o + row * (D * 2) + t * 2) = E::pack(sum * inv, nb * inv);
+    for (int i = 1; i < NG; ++i) M = fmaxf(M, gm[i]);
+    float dd = 0.f, aa = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (gm[i] == -INFINITY) continue;
+        const float w = fast_exp2((gm[i] - M) * kLog2e);
+        dd += w * gden[i];
+        aa += w * gacc[i][t];
+      }
+    }
+    const float inv = dd > 0.f ? 1.f / dd : 0.f;
+    const float nb = __shfl_down(aa, 1, 64);
+    if ((t & 1) == 0) *(uint32_t*)((unsigned char*)o + row * (D * 2) + t * 2) = E::pack(aa * inv, nb * inv);
+    if (t == 0) lse[row] = dd > 0.f ? M + logf(dd) : -INFINITY;
   }
-  if (t == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 template <class Tag, int D>
@@ -359,7 +384,7 @@ static hipError_t launch_splitkv_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((splitkv_kernel<Tag, D, CAUSAL>), dim3((unsigned)nblocks), dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine_t<Tag, D>(a.opart, a.lpart, a.o, a.lse, (long long)a.B * a.Hq * a.Nq, a.S4, stream);
+  return launch_combine_t<Tag, D>(a.opart, a.lpart, a.o, a.lse, (long long)a.B * a.Hq * a.Nq, a.S4 / 4, stream);
 }
 
 hipError_t launch_splitkv(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream) {

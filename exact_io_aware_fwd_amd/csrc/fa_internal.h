@@ -41,8 +41,8 @@ struct DecodeArgs {
   const void* v;
   void* o;
   float* lse;
-  float* opart;    // workspace: partial O per (row, split), [B*Hq*Nq, S4, d] fp32
-  float* lpart;    // workspace: partial LSE per (row, split), [B*Hq*Nq, S4] fp32 (natural log)
+  float* opart;    // workspace: partial O per (row, 4-split workgroup), [B*Hq*Nq, S4/4, d] fp32
+  float* lpart;    // workspace: partial LSE per (row, workgroup), [B*Hq*Nq, S4/4] fp32 (natural log)
   int B, Hq, Hkv, Nq, Nk;
   int RG;          // 32-row groups per (batch, K/V head): ceil(Hq/Hkv * Nq / 32)
   int C;           // keys per split (a multiple of 32)
@@ -75,10 +75,10 @@ inline SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int
   return p;
 }
 inline size_t splitkv_opart_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, const SplitPlan& p) {
-  return (size_t)((B * Hq * Nq * p.S4 * d * 4 + 255) / 256 * 256);
+  return (size_t)((B * Hq * Nq * (p.S4 / 4) * d * 4 + 255) / 256 * 256);
 }
 inline size_t splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, const SplitPlan& p) {
-  return splitkv_opart_bytes(B, Hq, Nq, d, p) + (size_t)((B * Hq * Nq * p.S4 * 4 + 255) / 256 * 256);
+  return splitkv_opart_bytes(B, Hq, Nq, d, p) + (size_t)((B * Hq * Nq * (p.S4 / 4) * 4 + 255) / 256 * 256);
 }
 
 // Return a hipError_t from the launches (hipSuccess when all were enqueued).

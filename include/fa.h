@@ -132,8 +132,9 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          struct ihipStream_t* stream);
 
 /*
- * Bytes of workspace fa_fwd_splitkv needs: per output row and split, the fp32 partial
- * O (d floats) and partial LSE, splits padded to a multiple of 4.  0 for invalid sizes.
+ * Bytes of workspace fa_fwd_splitkv needs: per output row and group of four splits
+ * (the splits padded to a multiple of 4), the fp32 partial O (d floats) and partial
+ * LSE.  0 for invalid sizes.
  */
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                                      fa_dtype dtype, int64_t num_splits);

@@ -142,13 +142,14 @@ def test_splitkv_empty_is_noop(L, kw):
 
 def test_splitkv_plan():
     # default splits: about 1024 waves over (batch, K/V head, 32-row group); each split a
-    # multiple of 32 keys; workspace = rows x splits (padded to 4) x (d + 1) floats
+    # multiple of 32 keys; a workgroup merges 4 splits, so the workspace holds
+    # rows x (splits padded to 4) / 4 x (d + 1) floats
     assert binding.splitkv_num_splits(1, 64, 8, 1, 65536, 128) == 128
     assert binding.splitkv_num_splits(2, 32, 8, 4, 8192, 128) == 64
     assert binding.splitkv_num_splits(1, 8, 2, 1, 40, 64) == 2      # at most one split per 32 keys
     ws = binding.splitkv_workspace_size(1, 64, 8, 1, 65536, 128, torch.bfloat16)
-    assert ws == 64 * 128 * 128 * 4 + 64 * 128 * 4
-    assert binding.splitkv_workspace_size(1, 8, 2, 1, 40, 64, torch.bfloat16, 3) == 8 * 4 * 64 * 4 + 256
+    assert ws == 64 * 32 * 128 * 4 + 64 * 32 * 4
+    assert binding.splitkv_workspace_size(1, 8, 2, 1, 40, 64, torch.bfloat16, 3) == 8 * 1 * 64 * 4 + 256
     assert binding.splitkv_workspace_size(1, 8, 3, 1, 40, 64, torch.bfloat16) == 0
 
 
