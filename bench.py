@@ -12,6 +12,7 @@ are under `passes`.  `cpu_baseline` times the fp64 oracle on a bounded sample
 of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--fwd-only]
+    python bench.py --decode [--steps K] ...    # split-KV decoding: GB/s against the HBM peak
 
 Profiling helpers (rocprofv3 runs of this same script):
     python bench.py --copy-calibration          # a plain 1 GiB device copy, for HBM counters
@@ -51,7 +52,10 @@ def parse():
     p.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 CSV output under DIR and exit")
     p.add_argument("--pmc", action="store_true", help="with --summarize: counter CSVs instead of kernel trace")
     p.add_argument("--record-traffic", nargs=3, metavar=("KERNEL_DIR", "COPY_DIR", "KERNEL_SUBSTR"),
-                   help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE runs and exit")
+                   help="write profiles/traffic.json from FETCH_SIZE/WRITE_SIZE runs and exit "
+                        "(SUBSTR may list alternatives separated by '|')")
+    p.add_argument("--decode", action="store_true",
+                   help="time the split-KV decoding forward instead (one JSON line, GB/s)")
     return p.parse_args()
 
 
@@ -60,6 +64,8 @@ KERNEL_SOURCES = {
             "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
     "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
             "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
+    "decode": ["exact_io_aware_fwd_amd/csrc/fa_decode.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
+               "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
@@ -118,7 +124,8 @@ def summarize(directory, pmc):
 
 def record_traffic(kdir, cdir, substr):
     # every kernel whose name contains substr runs once per call of the pass: sum them
-    kern = {k: v for k, v in pmc_per_dispatch(kdir).items() if substr in k}
+    alts = substr.split("|")
+    kern = {k: v for k, v in pmc_per_dispatch(kdir).items() if any(a in k for a in alts)}
     copy = {k: v for k, v in pmc_per_dispatch(cdir).items() if "copy" in k.lower()}
     if not kern or not copy:
         raise SystemExit(f"expected kernels matching {substr!r} and a copy kernel; got {list(kern)}, {list(copy)}")
@@ -128,7 +135,7 @@ def record_traffic(kdir, cdir, substr):
     kib = COPY_BYTES / 1024
     fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
     write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
-    kind = "bwd" if "bwd" in substr else "fwd"
+    kind = "decode" if ("splitkv" in substr or "combine" in substr) else "bwd" if "bwd" in substr else "fwd"
     data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
                   "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
@@ -180,6 +187,78 @@ def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
     }
 
 
+def bench_decode(args):
+    """Split-KV decoding on the long-cache decode workload: one JSON line in GB/s."""
+    import torch
+    import workloads
+    import exact_io_aware_fwd_amd as fa
+    from exact_io_aware_fwd_amd import metrics
+
+    w = workloads.DECODE_WORKLOADS[args.workload or workloads.DECODE_HEADLINE]
+    causal = True in w.causal
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu_inputs = workloads.make_decode_inputs(w)
+    q, k, v = (t.to(dev) for t in cpu_inputs)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.binding.splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, q.dtype), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fa.binding.fwd_splitkv(q, k, v, causal=causal, softmax_scale=w.scale, workspace=ws, out=o, lse=lse)
+
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 50)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = metrics.decode_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, q.element_size())
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "split-KV decoding attention: HBM GB/s and % of peak",
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
+        "ms_per_step": wall * 1e3 / steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16"}[q.dtype], "data": "synthetic (seeded iid N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": causal, "step": "fa_fwd_splitkv",
+                   "num_splits": fa.binding.splitkv_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": metrics.HBM_GBPS, "unit": "GB/s",
+                     "frac": gbps / metrics.HBM_GBPS, "traffic": traffic_bytes("decode"),
+                     "kernel": "splitkv_kernel + lse_combine_kernel", "avg_ms": ms, "algorithmic_bytes": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        qs, ks, vs = cpu_inputs
+        G = w.Hq // w.Hkv
+        tc = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - tc < 10.0:
+            oracle.attention_fwd_kv(qs[:1, :G], ks[:1, :1], vs[:1, :1], causal, w.scale)
+            reps += 1
+        dt = time.perf_counter() - tc
+        sb = metrics.decode_bytes(1, G, 1, w.Nq, w.Nk, w.d, q.element_size()) * reps
+        rec["cpu_baseline"] = {"value": sb / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                               "sample": f"batch 0, K/V head 0 with its {G} query heads, all {w.Nk} keys, "
+                                         f"numpy float64, repeated {reps} times in {dt:.1f} s; "
+                                         f"credited the same algorithmic bytes"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -195,6 +274,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        bench_decode(args)
+        return
 
     import torch
     import workloads

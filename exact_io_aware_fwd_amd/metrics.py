@@ -9,7 +9,9 @@ dS K, dS^T Q): 10 * B * Hq * N^2 * d, halved when causal.  The pages give no
 backward convention; this is the reading used throughout.
 
 Bytes: the compulsory HBM traffic of the forward pass is reading Q, K, V once and
-writing O and the fp32 log-sum-exp once.
+writing O and the fp32 log-sum-exp once.  Split-KV decoding is bound by that traffic
+(every cached K/V byte is read once per call; the arithmetic is small), so it is
+measured in bytes per second against the HBM peak.
 """
 from __future__ import annotations
 
@@ -36,3 +38,8 @@ def fwd_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elt_bytes: int) -> floa
 def bwd_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elt_bytes: int) -> float:
     """Compulsory backward traffic: Q, O, dO, dQ (Hq heads), K, V, dK, dV (Hkv heads), LSE."""
     return (4.0 * B * Hq + 4.0 * B * Hkv) * N * d * elt_bytes + 4.0 * B * Hq * N
+
+
+def decode_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, elt_bytes: int) -> float:
+    """Compulsory split-KV traffic: K, V (Nk rows) and Q read once, O and fp32 LSE written once."""
+    return 2.0 * B * Hkv * Nk * d * elt_bytes + 2.0 * B * Hq * Nq * d * elt_bytes + 4.0 * B * Hq * Nq
