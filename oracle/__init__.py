@@ -8,7 +8,8 @@ It is the plain, materialising definition of scaled dot-product attention writte
 out in numpy float64 (see :mod:`oracle.attention` for the passages each function
 follows), plus the footprint arithmetic of the pages' worked example, and the
 few-queries / long-key-sequence case with the log-sum-exp combine of split-KV
-decoding (:mod:`oracle.decode`).
+decoding (:mod:`oracle.decode`), and the FP8 path with per-block scales and the
+random-sign Hadamard transform (:mod:`oracle.fp8`).
 """
 from .attention import (
     attention_fwd,
@@ -18,6 +19,7 @@ from .attention import (
     to_f64,
 )
 from .decode import attention_fwd_kv, lse_combine
+from .fp8 import attention_fwd_fp8, quantize as fp8_quantize, dequantize as fp8_dequantize
 
 __all__ = [
     "attention_fwd",
@@ -27,4 +29,7 @@ __all__ = [
     "to_f64",
     "attention_fwd_kv",
     "lse_combine",
+    "attention_fwd_fp8",
+    "fp8_quantize",
+    "fp8_dequantize",
 ]

@@ -10,7 +10,9 @@ a single-head check, an 8-head d=64 fp16 case with the same shape and dtype as
 the flash-attention-sm75 README's usage example, a bf16 d=128 causal case with
 enlarged queries on half the heads, a grouped-query long-context case, and a
 forward+backward case.  Two decoding shapes (few queries, long key/value
-sequence) serve the split-KV forward.
+sequence) serve the split-KV forward.  The FP8 shapes add sparse outliers (a
+power-of-two multiple of a few entries, exact in bf16) and the random signs of the
+incoherent-processing transform, drawn here and passed to both sides.
 """
 from __future__ import annotations
 
@@ -148,3 +150,66 @@ def random_case(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype, wit
     if with_do:
         return q, k, v, randn(seed + 3, (B, Hq, N, d), dtype)
     return q, k, v
+
+
+@dataclass(frozen=True)
+class Fp8Workload:
+    """Forward attention through the FP8 path; inputs carry sparse outliers."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: tuple
+    seeds: tuple            # Q, K, V, signs
+    outlier_frac: float = 1e-3
+    outlier_mult: float = 16.0
+    block_q: int = 64
+    block_kv: int = 64
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# FP8 shapes: the headline grouped-query shape, an 8-head d=128 case the oracle finishes
+# in seconds (causal and not), and a d=64 case with a ragged tail (N = 1000).  Inputs are
+# N(0,1) in bf16 with 0.1% of the entries multiplied by 16: the pages motivate the
+# transform by outliers without giving a distribution, so this recipe is a choice.
+FP8_WORKLOADS = {
+    "fp8_gqa_b2_hq32_hkv8_n8192_d128_causal": Fp8Workload(
+        "fp8_gqa_b2_hq32_hkv8_n8192_d128_causal", 2, 32, 8, 8192, 128, (True,), (8100, 8101, 8102, 8103),
+        note="the grouped-query long-context shape through the FP8 path"),
+    "fp8_mha8_n1024_d128": Fp8Workload(
+        "fp8_mha8_n1024_d128", 1, 8, 8, 1024, 128, (False, True), (8000, 8001, 8002, 8003),
+        note="8 heads, causal and not on the same inputs"),
+    "fp8_h4_n1000_d64": Fp8Workload(
+        "fp8_h4_n1000_d64", 1, 4, 2, 1000, 64, (False, True), (8200, 8201, 8202, 8203),
+        note="d = 64, two query heads per K/V head, a ragged last block"),
+}
+FP8_HEADLINE = "fp8_gqa_b2_hq32_hkv8_n8192_d128_causal"
+
+
+def randn_outliers(seed: int, shape, frac: float, mult: float, dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0,1) from PCG64(seed) in float32, a `frac` share of entries (chosen by the same
+    generator) multiplied by `mult`, rounded (RNE) to `dtype`."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=tuple(shape), dtype=np.float32)
+    x[g.random(size=tuple(shape), dtype=np.float32) < frac] *= np.float32(mult)
+    return torch.from_numpy(x).to(dtype)
+
+
+def random_signs(seed: int, d: int) -> np.ndarray:
+    """d values of +-1 (float32) from PCG64(seed)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return (g.integers(0, 2, size=d) * 2 - 1).astype(np.float32)
+
+
+def make_fp8_inputs(w: Fp8Workload, N: int | None = None):
+    """CPU tensors q [B,Hq,N,d], k, v [B,Hkv,N,d] (bf16) and the signs (numpy float32 [d])."""
+    N = w.N if N is None else N
+    f, m = w.outlier_frac, w.outlier_mult
+    return (randn_outliers(w.seeds[0], (w.B, w.Hq, N, w.d), f, m), randn_outliers(w.seeds[1], (w.B, w.Hkv, N, w.d), f, m),
+            randn_outliers(w.seeds[2], (w.B, w.Hkv, N, w.d), f, m), random_signs(w.seeds[3], w.d))
