@@ -3,6 +3,8 @@
     import exact_io_aware_fwd_amd as fa
     o, lse = fa.fwd(q, k, v, causal=True)                 # q [B,Hq,N,d], k/v [B,Hkv,N,d]
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    o, lse = fa.fwd_splitkv(q_new, k_cache, v_cache, causal=True)   # few queries, long cache
+    o, lse = fa.fwd_fp8(*fa.fp8_prepare(q, k, v, signs), causal=True)  # FP8 path
 """
 from .binding import (  # noqa: F401
     FA_BF16,
@@ -15,8 +17,16 @@ from .binding import (  # noqa: F401
     bwd,
     bwd_workspace_size,
     declared_symbols,
+    fp8_prepare,
+    fp8_quantize,
+    fp8_quantize_v,
     fwd,
+    fwd_fp8,
+    fwd_splitkv,
     last_error,
+    lse_combine,
     load,
+    splitkv_num_splits,
+    splitkv_workspace_size,
     status_string,
 )

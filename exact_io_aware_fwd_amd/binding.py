@@ -59,6 +59,15 @@ def load() -> ctypes.CDLL:
     L.fa_fwd_splitkv_num_splits.restype = _i64
     L.fa_lse_combine.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
     L.fa_lse_combine.restype = ctypes.c_int
+    L.fa_fp8_v_codes_bytes.argtypes = [_i64, _i64, _i64, _i64]
+    L.fa_fp8_v_codes_bytes.restype = ctypes.c_size_t
+    L.fa_fp8_quantize_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _i64, _vp]
+    L.fa_fp8_quantize_rows.restype = ctypes.c_int
+    L.fa_fp8_quantize_v.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _i64, _vp]
+    L.fa_fp8_quantize_v.restype = ctypes.c_int
+    L.fa_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                             ctypes.c_int, ctypes.c_float, _vp]
+    L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -238,3 +247,100 @@ def lse_combine(o_parts: torch.Tensor, lse_parts: torch.Tensor, dtype=torch.bflo
     if st != FA_OK:
         _raise(st)
     return o, lse
+
+
+def fp8_quantize(x: torch.Tensor, block_rows: int = 64, signs: torch.Tensor | None = None):
+    """Block-quantise rows of x [B,H,N,d] (fp16/bf16) to e4m3 via fa_fp8_quantize_rows.
+
+    signs: d float32 values of +-1 on x's device (the random-sign Hadamard transform is
+    applied first), or None.  Returns (codes uint8 [B,H,N,d], scales float32
+    [B,H,ceil(N/block_rows)]).
+    """
+    L = load()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    dev = x.device
+    _check(x, "x", dev)
+    if signs is not None:
+        _check(signs, "signs", dev, torch.float32)
+        if signs.shape != (d,):
+            raise ValueError(f"signs must be [{d}]")
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, -(-N // block_rows)), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fp8_quantize_rows(x.data_ptr(), None if signs is None else signs.data_ptr(), codes.data_ptr(),
+                                    scales.data_ptr(), B, H, N, d, _dtype_code(x), block_rows, stream)
+    if st != FA_OK:
+        _raise(st)
+    return codes, scales
+
+
+def fp8_quantize_v(v: torch.Tensor, block_rows: int = 64):
+    """Block-quantise values v [B,H,N,d] to e4m3 in the value-tile layout via fa_fp8_quantize_v.
+
+    Returns (codes uint8 [B,H,ceil(N/64),d,64], scales float32 [B,H,ceil(N/block_rows)]).
+    """
+    L = load()
+    if v.dim() != 4:
+        raise ValueError("v must be [B, H, N, d]")
+    B, H, N, d = v.shape
+    dev = v.device
+    _check(v, "v", dev)
+    codes = torch.empty((B, H, -(-N // 64), d, 64), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, -(-N // block_rows)), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fp8_quantize_v(v.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d, _dtype_code(v),
+                                 block_rows, stream)
+    if st != FA_OK:
+        _raise(st)
+    return codes, scales
+
+
+def fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scales, causal: bool = False, softmax_scale: float | None = None,
+            block_q: int = 64, block_kv: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """O (bf16), LSE = FP8 attention over quantised operands via fa_fwd_fp8.
+
+    q8 [B,Hq,N,d] and k8 [B,Hkv,N,d] from fp8_quantize, v8 [B,Hkv,ceil(N/64),d,64] from
+    fp8_quantize_v, with their scales and block sizes.
+    """
+    L = load()
+    if q8.dim() != 4 or k8.dim() != 4 or v8.dim() != 5:
+        raise ValueError("q8, k8 must be [B, H, N, d] and v8 [B, H, ceil(N/64), d, 64]")
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if k8.shape != (B, Hkv, N, d) or v8.shape != (B, Hkv, -(-N // 64), d, 64):
+        raise ValueError("k8 / v8 shapes do not match q8")
+    dev = q8.device
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check(t, n, dev, torch.uint8)
+    for t, n, blk, H in ((q_scales, "q_scales", block_q, Hq), (k_scales, "k_scales", block_kv, Hkv),
+                         (v_scales, "v_scales", block_kv, Hkv)):
+        _check(t, n, dev, torch.float32)
+        if t.shape != (B, H, -(-N // blk)):
+            raise ValueError(f"{n} must be [{B}, {H}, {-(-N // blk)}]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(o, "out", dev, torch.bfloat16)
+    _check(lse_t, "lse", dev, torch.float32)
+    if o.shape != (B, Hq, N, d) or lse_t.shape != (B, Hq, N):
+        raise ValueError("out/lse have the wrong shape")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scales.data_ptr(), k_scales.data_ptr(),
+                          v_scales.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, Hq, Hkv, N, d, block_q, block_kv,
+                          int(bool(causal)), scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return o, lse_t
+
+
+def fp8_prepare(q, k, v, signs=None, block_q: int = 64, block_kv: int = 64):
+    """Quantise q, k (transformed when signs is given) and v for fwd_fp8; returns the six operands."""
+    q8, qs = fp8_quantize(q, block_q, signs)
+    k8, ks = fp8_quantize(k, block_kv, signs)
+    v8, vs = fp8_quantize_v(v, block_kv)
+    return q8, k8, v8, qs, ks, vs

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fp8_quant.hip", "fa_fwd_fp8.hip"]
 # Per-source flags.  The backward kernels keep their long-lived accumulators in AGPRs
 # through inline-asm MFMAs; every other MFMA is asked to write VGPRs, which is where
 # the elementwise code reads S and dP (otherwise the compiler may place those results

@@ -100,6 +100,73 @@ fa_status check_splitkv_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
 
 }  // namespace
 
+namespace {
+
+bool fp8_block_ok(int64_t b) { return b == 64 || b == 128 || b == 256; }
+int log2_block(int64_t b) { return b == 64 ? 6 : b == 128 ? 7 : 8; }
+
+// The fp64 value nearest 1/sqrt(d) for d a power of two: 2^(-k/2) for even k = log2 d,
+// else the fp64 value nearest sqrt(2) times 2^(-(k+1)/2) (scaling by 2^j commutes
+// with rounding, and sqrt is correctly rounded).
+double inv_sqrt_pow2(int64_t d) {
+  int k = 0;
+  while ((int64_t(1) << k) < d) ++k;
+  return (k % 2 == 0) ? std::ldexp(1.0, -k / 2) : std::ldexp(std::sqrt(2.0), -(k + 1) / 2);
+}
+
+fa_status check_ptr4(const void* p, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+  return FA_OK;
+}
+
+// Size checks of the FP8 quantisers.  Sets *empty when there is nothing to do.
+fa_status check_fp8_quant(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype, int64_t block_rows,
+                          bool* empty) {
+  if (B < 0 || N < 0) return fail(FA_ERR_INVALID_ARGUMENT, "B and N must be >= 0 (B=%lld N=%lld)", (long long)B,
+                                  (long long)N);
+  if (H < 1) return fail(FA_ERR_INVALID_ARGUMENT, "H must be >= 1 (H=%lld)", (long long)H);
+  if (d < 1) return fail(FA_ERR_INVALID_ARGUMENT, "d must be >= 1 (d=%lld)", (long long)d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                                       (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!fp8_block_ok(block_rows))
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_rows must be 64, 128 or 256 (got %lld)", (long long)block_rows);
+  if (B > INT_MAX || H > INT_MAX || N > INT_MAX / 2 || B * H > INT_MAX || N * d > INT_MAX)
+    return fail(FA_ERR_INVALID_ARGUMENT, "sizes exceed the supported index range");
+  const int64_t nblk = (N + block_rows - 1) / block_rows;
+  if (B * H > 0 && nblk > (int64_t)UINT_MAX / (B * H))
+    return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
+  *empty = (B == 0 || N == 0);
+  return FA_OK;
+}
+
+fa_status run_fp8_quant(const void* x, const float* signs, void* codes, float* scales, int64_t B, int64_t H,
+                        int64_t N, int64_t d, fa_dtype dtype, int64_t block_rows, int mode, hipStream_t stream) {
+  bool empty = false;
+  fa_status st = check_fp8_quant(B, H, N, d, dtype, block_rows, &empty);
+  if (st != FA_OK || empty) return st;
+  if ((st = check_ptr(x, "x")) != FA_OK || (st = check_ptr(codes, "codes")) != FA_OK ||
+      (st = check_ptr4(scales, "scales")) != FA_OK)
+    return st;
+  if (mode == 0 && (st = check_ptr4(signs, "signs")) != FA_OK) return st;
+  fa::QuantArgs a;
+  a.x = x;
+  a.signs = signs;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = scales;
+  a.BH = (int)(B * H);
+  a.N = (int)N;
+  a.block_rows = (int)block_rows;
+  a.nblk = (int)((N + block_rows - 1) / block_rows);
+  a.inv_sqrt_d = inv_sqrt_pow2(d);
+  const hipError_t err = fa::launch_fp8_quant(a, (int)d, dtype == FA_BF16, mode, stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "quantisation launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fa_status_string(fa_status s) {
@@ -272,6 +339,63 @@ fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, 
   const hipError_t err = fa::launch_lse_combine(o_parts, lse_parts, o, lse, (long long)rows, (int)num_parts, (int)d,
                                                 dtype == FA_BF16, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+size_t fa_fp8_v_codes_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return 0;
+  return (size_t)(B * H * ((N + 63) / 64) * d * 64);
+}
+
+fa_status fa_fp8_quantize_rows(const void* x, const float* signs, void* codes, float* scales, int64_t B,
+                               int64_t H, int64_t N, int64_t d, fa_dtype dtype, int64_t block_rows,
+                               struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  return run_fp8_quant(x, signs, codes, scales, B, H, N, d, dtype, block_rows, signs ? 0 : 1, (hipStream_t)stream);
+}
+
+fa_status fa_fp8_quantize_v(const void* x, void* codes, float* scales, int64_t B, int64_t H, int64_t N, int64_t d,
+                            fa_dtype dtype, int64_t block_rows, struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  return run_fp8_quant(x, nullptr, codes, scales, B, H, N, d, dtype, block_rows, 2, (hipStream_t)stream);
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scales, const float* k_scales,
+                     const float* v_scales, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                     int64_t d, int64_t block_q, int64_t block_kv, int causal, float softmax_scale,
+                     struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = check_sizes(B, Hq, Hkv, N, d, FA_BF16, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (!fp8_block_ok(block_q) || !fp8_block_ok(block_kv))
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_q and block_kv must be 64, 128 or 256 (got %lld, %lld)",
+                (long long)block_q, (long long)block_kv);
+  if (empty) return FA_OK;
+  if ((st = check_ptr(q8, "q8")) != FA_OK || (st = check_ptr(k8, "k8")) != FA_OK ||
+      (st = check_ptr(v8, "v8")) != FA_OK || (st = check_ptr4(q_scales, "q_scales")) != FA_OK ||
+      (st = check_ptr4(k_scales, "k_scales")) != FA_OK || (st = check_ptr4(v_scales, "v_scales")) != FA_OK ||
+      (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK)
+    return st;
+  fa::Fp8FwdArgs a;
+  a.q = static_cast<const uint8_t*>(q8);
+  a.k = static_cast<const uint8_t*>(k8);
+  a.v = static_cast<const uint8_t*>(v8);
+  a.qs = q_scales;
+  a.ks = k_scales;
+  a.vs = v_scales;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.N = (int)N;
+  a.qshift = log2_block(block_q);
+  a.kvshift = log2_block(block_kv);
+  a.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t err = fa::launch_fwd_fp8(a, (int)d, causal != 0, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "FP8 forward launch failed: %s", hipGetErrorString(err));
   return FA_OK;
 }
 

@@ -81,10 +81,39 @@ inline size_t splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t
   return splitkv_opart_bytes(B, Hq, Nq, d, p) + (size_t)((B * Hq * Nq * (p.S4 / 4) * 4 + 255) / 256 * 256);
 }
 
+// FP8 block quantisation: one workgroup of block_rows * d / 32 threads per scale block.
+struct QuantArgs {
+  const void* x;        // [B, H, N, d] fp16/bf16
+  const float* signs;   // [d] of +-1 (transform) or null
+  uint8_t* codes;       // rows: [B, H, N, d]; value tiles: [B, H, ceil(N/64), d, 64]
+  float* scales;        // [B, H, nblk] powers of two
+  int BH, N, block_rows, nblk;
+  double inv_sqrt_d;    // the fp64 value nearest 1/sqrt(d)
+};
+
+// FP8 forward: codes and power-of-two block scales of the transformed Q and K and of V
+// (value tiles as written by the quantiser), bf16 output.
+struct Fp8FwdArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N;
+  int qshift, kvshift;  // log2 of the query and key/value block rows
+  float scale_log2;     // softmax scale * log2(e)
+};
+
 // Return a hipError_t from the launches (hipSuccess when all were enqueued).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_splitkv(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_fp8_quant(const QuantArgs& a, int d, bool bf16, int mode, hipStream_t stream);  // mode 0: rows
+                                                                                                 // + transform, 1: rows, 2: value tiles
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, float* lse, long long rows, int S,
                               int d, bool bf16, hipStream_t stream);
 

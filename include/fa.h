@@ -161,6 +161,55 @@ fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, 
                          int64_t rows, int64_t num_parts, int64_t d, fa_dtype dtype,
                          struct ihipStream_t* stream);
 
+/*
+ * FP8 (e4m3) forward pass with per-block scales and incoherent processing.
+ *
+ * "Flash Attention" (wiki), section "FlashAttention-3": block quantization plus a
+ * transform of random signs and a Hadamard matrix applied to queries and keys (the
+ * same orthogonal transform on both leaves Q K^T unchanged in exact arithmetic and
+ * spreads outliers over all coordinates); the explainer "What Hopper bought
+ * FlashAttention-3": accuracy kept by per-block scaling.  Two steps: quantise Q and K
+ * (with the transform) and V once, then run the forward pass on the codes.
+ *
+ * Quantisation.  x [B,H,N,d] of `dtype` (16-byte aligned); signs: d floats of +1/-1
+ * on the device, or NULL for no transform.  With signs, each row becomes
+ * x diag(signs) H_d / sqrt(d) (H_d the Sylvester Hadamard matrix), formed exactly in
+ * fp64 with one fp64 multiplication by the fp64 value nearest 1/sqrt(d), then rounded
+ * to fp32.  Every block of block_rows consecutive rows of a head (64, 128 or 256; the
+ * last block may be short) gets the power-of-two scale 2^e, e the smallest integer
+ * with max|value| <= 448 * 2^e (e = 0 for an all-zero block), and the codes are
+ * e4m3(value / 2^e), rounded to nearest even.  Non-finite inputs, or values past the
+ * fp32 range after the transform, give unspecified codes.
+ *   fa_fp8_quantize_rows: codes [B,H,N,d] bytes (16-byte aligned), scales float
+ *       [B,H,ceil(N/block_rows)] (4-byte aligned).  For queries and keys.
+ *   fa_fp8_quantize_v:    codes in the value-tile layout [B,H,ceil(N/64),d,64] bytes
+ *       (fa_fp8_v_codes_bytes): per 64-key tile the transposed [d][64] block, keys
+ *       permuted so that position 32h + 16t + 4a + b holds key 32t + 8a + 4h + b;
+ *       keys past N are code 0.  Scales as above.  No transform.
+ *
+ * fa_fwd_fp8.  q8 [B,Hq,N,d] and k8 [B,Hkv,N,d] row codes, v8 value tiles of
+ * [B,Hkv,N,d], their scales with block sizes block_q and block_kv (64, 128 or 256;
+ * scales must be powers of two, as the quantisers write them); o [B,Hq,N,d] bf16,
+ * lse [B,Hq,N] float32 (natural log).  S = softmax_scale * Q' K'^T over the
+ * dequantised codes (scale * value); P is rounded to e4m3 for the product with V
+ * (P <= 256 by the rescaling threshold); the row sums behind O's normalisation and
+ * the LSE use the unrounded fp32 P.  Grouping and causal masking as in fa_fwd.
+ * Outputs are deterministic.  Buffers are the caller's; nothing is allocated.
+ */
+size_t fa_fp8_v_codes_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+fa_status fa_fp8_quantize_rows(const void* x, const float* signs, void* codes, float* scales, int64_t B,
+                               int64_t H, int64_t N, int64_t d, fa_dtype dtype, int64_t block_rows,
+                               struct ihipStream_t* stream);
+
+fa_status fa_fp8_quantize_v(const void* x, void* codes, float* scales, int64_t B, int64_t H, int64_t N, int64_t d,
+                            fa_dtype dtype, int64_t block_rows, struct ihipStream_t* stream);
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scales, const float* k_scales,
+                     const float* v_scales, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                     int64_t d, int64_t block_q, int64_t block_kv, int causal, float softmax_scale,
+                     struct ihipStream_t* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 

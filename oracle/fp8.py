@@ -68,22 +68,30 @@ def e4m3_values() -> np.ndarray:
 
 
 _TABLE = e4m3_values()
-_POS = _TABLE[:127]            # codes 0 .. 126: the non-negative finite values, increasing
 
 
 def e4m3_encode(x) -> np.ndarray:
-    """Round float64 values with |x| <= 448 to the nearest e4m3 code (ties to even)."""
+    """Round float64 values with |x| <= 448 to the nearest e4m3 code (ties to even).
+
+    The e4m3 values in [2^E, 2^(E+1)) (E >= -6) are spaced 2^(E-3) apart, and those
+    below 2^-6 are the multiples of 2^-9; |x| divided by its spacing (exact: a power of
+    two) is rounded to the nearest integer, ties to the even one, which is the value's
+    significand in units of the spacing, so its parity is the code's last bit.
+    """
     x = np.asarray(x, dtype=np.float64)
     if not np.all(np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
         raise ValueError("e4m3_encode needs finite values with |x| <= 448")
     a = np.abs(x)
-    hi = np.searchsorted(_POS, a, side="left")          # _POS[hi-1] < a <= _POS[hi]
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    dlo, dhi = a - _POS[lo], _POS[hi] - a
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a == _POS[hi], hi, code)            # exact hits (also a == 0)
+    _, e = np.frexp(a)                                  # a = m 2^e, m in [0.5, 1)
+    E = np.maximum(e - 1, -6)                           # binade of a; the subnormals share 2^-6's spacing
+    step = np.ldexp(1.0, E - 3)
+    n = np.rint(a / step)                               # round half to even
+    r = n * step                                        # the chosen e4m3 magnitude
+    _, er = np.frexp(r)
+    Er = er - 1
+    normal = r >= 2.0 ** -6
+    man = np.where(normal, np.rint(np.ldexp(r, -Er) * 8) - 8, np.rint(r * 2.0 ** 9))
+    code = np.where(normal, (Er + 7) * 8 + man, man).astype(np.int64)
     code = code | np.where(np.signbit(x), 0x80, 0)
     return code.astype(np.uint8)
 

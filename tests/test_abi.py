@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol(L):
     names = binding.declared_symbols()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
                           "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_num_splits",
-                          "fa_lse_combine"}
+                          "fa_lse_combine", "fa_fp8_v_codes_bytes", "fa_fp8_quantize_rows", "fa_fp8_quantize_v",
+                          "fa_fwd_fp8"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -159,3 +160,54 @@ def test_splitkv_plan():
 ])
 def test_lse_combine_validation(L, args, expect):
     assert L.fa_lse_combine(*args, None) == expect
+
+
+def quant_rows(L, x=P, signs=P, codes=P, scales=P, B=1, H=2, N=100, d=128, dtype=1, blk=64):
+    return L.fa_fp8_quantize_rows(x, signs, codes, scales, B, H, N, d, dtype, blk, None)
+
+
+def quant_v(L, x=P, codes=P, scales=P, B=1, H=2, N=100, d=128, dtype=1, blk=64):
+    return L.fa_fp8_quantize_v(x, codes, scales, B, H, N, d, dtype, blk, None)
+
+
+def fwd_fp8(L, B=1, Hq=2, Hkv=1, N=100, d=128, bq=64, bkv=64, causal=0, scale=0.125, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "qs", "ks", "vs", "o", "lse")}
+    p.update(ptrs)
+    return L.fa_fwd_fp8(p["q"], p["k"], p["v"], p["qs"], p["ks"], p["vs"], p["o"], p["lse"], B, Hq, Hkv, N, d,
+                        bq, bkv, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), INV), (dict(codes=P + 8), INV), (dict(scales=P + 2), INV), (dict(blk=32), INV),
+    (dict(blk=96), INV), (dict(d=96), UNS), (dict(dtype=7), UNS), (dict(H=0), INV), (dict(N=-1), INV),
+    (dict(N=1 << 31), INV),
+])
+def test_fp8_quantize_rejects(L, kw, expect):
+    assert quant_rows(L, **kw) == expect
+    assert binding.last_error() != ""
+    kw.pop("signs", None)
+    assert quant_v(L, **kw) == expect
+
+
+def test_fp8_quantize_signs_optional_and_empty(L):
+    # a NULL sign vector means no transform (it is not an error); empty inputs are no-ops
+    assert quant_rows(L, N=0, signs=None) == OK
+    assert quant_rows(L, B=0) == OK and quant_v(L, B=0) == OK
+    assert quant_rows(L, signs=P + 2) == INV      # present but misaligned
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INV), (dict(vs=None), INV), (dict(o=P + 4), INV), (dict(bq=32), INV), (dict(bkv=512), INV),
+    (dict(Hq=3, Hkv=2), INV), (dict(d=256), UNS), (dict(scale=-1.0), INV), (dict(N=-5), INV),
+])
+def test_fwd_fp8_rejects(L, kw, expect):
+    assert fwd_fp8(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+def test_fwd_fp8_empty_and_sizes(L):
+    assert fwd_fp8(L, N=0, q=None) == OK and fwd_fp8(L, B=0) == OK
+    # value tiles: 64 keys x d bytes per tile, tiles rounded up
+    assert L.fa_fp8_v_codes_bytes(2, 3, 100, 128) == 2 * 3 * 2 * 128 * 64
+    assert L.fa_fp8_v_codes_bytes(1, 1, 64, 64) == 64 * 64
+    assert L.fa_fp8_v_codes_bytes(1, 1, 0, 64) == 0

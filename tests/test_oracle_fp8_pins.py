@@ -216,7 +216,8 @@ def test_fp8_oracle_pins(pin):
 
 
 MUTANTS = {
-    "ties_away_from_zero": ("((dhi == dlo) & (hi % 2 == 0))", "(dhi == dlo)"),
+    "ties_away_from_zero": ("n = np.rint(a / step)", "n = np.floor(a / step + 0.5)"),
+    "subnormal_spacing_2e_minus_10": ("np.rint(r * 2.0 ** 9)", "np.rint(r * 2.0 ** 10)"),
     "fnuz_bias_8": ("2.0 ** (exp.astype(np.float64) - 7)", "2.0 ** (exp.astype(np.float64) - 8)"),
     "hadamard_other_sign": ("H = np.block([[H, H], [H, -H]])", "H = np.block([[H, H], [-H, H]])"),
     "normalised_by_1_over_d": ("return ((X * s) @ hadamard(d)) * inv_sqrt(d)", "return ((X * s) @ hadamard(d)) / d"),
