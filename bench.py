@@ -13,6 +13,7 @@ of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--fwd-only]
     python bench.py --decode [--steps K] ...    # split-KV decoding: GB/s against the HBM peak
+    python bench.py --fp8 [--steps K] ...       # FP8 forward (quantise + attention): TFLOP/s
 
 Profiling helpers (rocprofv3 runs of this same script):
     python bench.py --copy-calibration          # a plain 1 GiB device copy, for HBM counters
@@ -56,6 +57,8 @@ def parse():
                         "(SUBSTR may list alternatives separated by '|')")
     p.add_argument("--decode", action="store_true",
                    help="time the split-KV decoding forward instead (one JSON line, GB/s)")
+    p.add_argument("--fp8", action="store_true",
+                   help="time the FP8 forward (block quantisation with the Hadamard transform + attention)")
     return p.parse_args()
 
 
@@ -66,6 +69,8 @@ KERNEL_SOURCES = {
             "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
     "decode": ["exact_io_aware_fwd_amd/csrc/fa_decode.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
                "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
+    "fp8": ["exact_io_aware_fwd_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
+            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
@@ -135,7 +140,8 @@ def record_traffic(kdir, cdir, substr):
     kib = COPY_BYTES / 1024
     fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
     write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
-    kind = "decode" if ("splitkv" in substr or "combine" in substr) else "bwd" if "bwd" in substr else "fwd"
+    kind = ("decode" if ("splitkv" in substr or "combine" in substr) else "fp8" if "fp8" in substr
+            else "bwd" if "bwd" in substr else "fwd")
     data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
                   "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
@@ -259,6 +265,96 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_fp8(args):
+    """FP8 forward on the grouped-query N=8192 shape: one JSON line in TFLOP/s.
+
+    A step quantises Q and K (random-sign Hadamard transform, per-block scales) and V,
+    then runs the FP8 attention forward; `value` credits the forward's algorithmic FLOPs
+    to the whole step.  The roofline line is the attention kernel against the dense
+    FP8 matrix-core peak."""
+    import torch
+    import workloads
+    import exact_io_aware_fwd_amd as fa
+    from exact_io_aware_fwd_amd import metrics
+
+    w = workloads.FP8_WORKLOADS[args.workload or workloads.FP8_HEADLINE]
+    causal = True in w.causal
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu_inputs = workloads.make_fp8_inputs(w)
+    q, k, v = (t.to(dev) for t in cpu_inputs[:3])
+    signs = torch.from_numpy(cpu_inputs[3]).to(dev)
+    o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    ops = [None]
+
+    def quantise():
+        ops[0] = fa.fp8_prepare(q, k, v, signs, w.block_q, w.block_kv)
+
+    def attend():
+        fa.fwd_fp8(*ops[0], causal=causal, softmax_scale=w.scale, block_q=w.block_q, block_kv=w.block_kv,
+                   out=o, lse=lse)
+
+    for _ in range(max(args.warmup, 3)):
+        quantise()
+        attend()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        quantise()
+        ev[i][1].record(stream)
+        attend()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    a_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    flops = metrics.fwd_flops(w.B, w.Hq, w.N, w.d, causal)
+    step_ms = q_ms + a_ms
+    value = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (a_ms * 1e-3) / 1e12
+    qbytes = metrics.fp8_quant_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, 2, w.block_q, w.block_kv)
+    rec = {
+        "metric": "FP8 attention forward TFLOPS and % of the FP8 matrix-core peak at N=8192 d=128 causal",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, 3),
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 operands, fp32 accumulation, bf16 output",
+        "data": "synthetic (seeded N(0,1), 0.1% of entries x16; random signs)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": causal,
+                   "block_q": w.block_q, "block_kv": w.block_kv,
+                   "step": "fa_fp8_quantize_rows (Q, K) + fa_fp8_quantize_v + fa_fwd_fp8"},
+        "passes": {"quantise_ms": q_ms, "quantise_GBps": qbytes / (q_ms * 1e-3) / 1e9,
+                   "attention_ms": a_ms, "attention_TFLOPs": achieved},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": metrics.MFMA_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / metrics.MFMA_FP8_TFLOPS, "traffic": traffic_bytes("fp8"),
+                     "kernel": "fwd_fp8_kernel", "avg_ms": a_ms, "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        qc, kc, vc, sc = cpu_inputs
+        G = w.Hq // w.Hkv
+        heads = max(G, min(args.cpu_heads, w.Hq) // G * G)
+        t1 = time.perf_counter()
+        oracle.attention_fwd_fp8(qc[:1, :heads], kc[:1, :heads // G], vc[:1, :heads // G], sc, causal, w.scale,
+                                 w.block_q, w.block_kv)
+        dt = time.perf_counter() - t1
+        sflops = metrics.fwd_flops(1, heads, w.N, w.d, causal)
+        rec["cpu_baseline"] = {"value": sflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                               "sample": f"batch 0, query heads 0-{heads - 1} with their K/V heads, all {w.N} rows: "
+                                         f"quantisation and float64 attention of the dequantised operands "
+                                         f"(full N^2 even when causal; credited the same algorithmic FLOPs); "
+                                         f"{dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -274,6 +370,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.fp8:
+        bench_fp8(args)
+        return
     if args.decode:
         bench_decode(args)
         return

@@ -118,14 +118,6 @@ static __device__ __forceinline__ void acc_drain(f32x16 (&acc)[N]) {
 #endif
 }
 
-// Keep an accumulator in AGPRs across a VALU update (the compiler inserts the moves).
-template <class T>
-static __device__ __forceinline__ void opaque_a(T& x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" : "+a"(x));
-#endif
-}
-
 static __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -4,7 +4,8 @@
 // Method: "Flash Attention" (wiki), section "FlashAttention-3" — block quantization
 // plus incoherent processing (random signs and a Hadamard transform, the same
 // orthogonal transform for queries and keys, so their dot products are unchanged);
-// "What Hopper bought FlashAttention-3" — per-block scaling.
+// "FlashAttention" (explainer), section "What Hopper bought FlashAttention-3" —
+// per-block scaling.
 //
 // Definition implemented (the readings where the pages are silent):
 //  * x -> x M with M = diag(sigma) H_d / sqrt(d), H_d the Sylvester Hadamard matrix.

@@ -1,10 +1,10 @@
 // FP8 (e4m3) forward pass of attention for gfx950: both products on the FP8 matrix
 // core, online softmax in fp32, O (bf16) and LSE (fp32) out.
 //
-// Method: "Flash Attention" (wiki), section "FlashAttention-3" and the explainer "What
-// Hopper bought FlashAttention-3": FP8 operands with per-block scales, queries and
-// keys taken through the random-sign Hadamard transform beforehand (the quantiser in
-// fa_fp8_quant.hip).  The tiling and the online softmax are the forward pass of
+// Method: "Flash Attention" (wiki), section "FlashAttention-3", and "FlashAttention"
+// (explainer), section "What Hopper bought FlashAttention-3": FP8 operands with
+// per-block scales, queries and keys taken through the random-sign Hadamard transform
+// beforehand (the quantiser in fa_fp8_quant.hip).  The tiling and the online softmax are the forward pass of
 // "FlashAttention Primer: IO-Aware Attention, from FA1 to FA4", section
 // "FlashAttention-1: tiling plus online softmax", with the work split of its
 // "FlashAttention-2" section and the conditional rescaling of its "FlashAttention-4"
@@ -225,13 +225,15 @@ __global__ void __launch_bounds__(512) fwd_fp8_kernel(const Fp8FwdArgs a) {
     bool raise;
   };
 
-  // S-phase of unit u: NSL slots, each with EPS of unit u's exponentials (and their
-  // row-sum adds), then one score product of unit u+1 (K from sln).  The K fragments
-  // are read PD slots ahead, the first ones at the start of the phase, so the
-  // exponentials cover the LDS latency.  Ends with P packed to e4m3 (the B operand of
-  // the value products) and O rescaled if unit u moved the reference.
+  // S-phase of unit u.  First O is rescaled if unit u moved the reference (a branch at
+  // the start, so that nothing issued later in the phase is sunk past it).  Then NSL
+  // slots, each with EPS of unit u's exponentials (and their row-sum adds) followed by
+  // one score product of unit u+1 (K from sln, read PD slots ahead, the first ones at
+  // the start of the phase, so the exponentials cover the LDS latency).  Ends with P
+  // packed to e4m3, the B operand of the value products.
   auto sphase = [&](const unsigned char* sln, f32x16 (&sc)[2], f32x16 (&sn)[2], int skn, const Ref& rf,
                     float& rs) __attribute__((always_inline)) -> u32x8 {
+    if (__builtin_amdgcn_ballot_w64(rf.raise) != 0) rescale(rf.alpha);
     u32x8 kf[NSL];
 #pragma unroll
     for (int i = 0; i < PD; ++i) kf[i] = kread(sln, i);
@@ -260,32 +262,41 @@ __global__ void __launch_bounds__(512) fwd_fp8_kernel(const Fp8FwdArgs a) {
       }
     const u32x8 pf = u32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
     keep(pf);
-    if (__builtin_amdgcn_ballot_w64(rf.raise) != 0) rescale(rf.alpha);
     __builtin_amdgcn_sched_barrier(0);
     return pf;
   };
   // PV-phase of unit u: NE slots, each one value product (V from slc, read PD slots
-  // ahead); meanwhile the row max of unit u+1 (masked under MASK) picks its reference.
+  // ahead) after a share of the row max of unit u+1 (masked under MASK): tile 0's
+  // scores in the first slot, tile 1's (the last product of the S-phase) in the second,
+  // the new reference in the third (the second for d = 64).
   auto pphase = [&](auto MASK, int u, const unsigned char* slc, f32x16 (&sn)[2], int svc, Ref& rf,
                     const u32x8& pf) __attribute__((always_inline)) {
     u32x8 vf[NE];
 #pragma unroll
     for (int i = 0; i < PD; ++i) vf[i] = vread(slc, i);
     float mx = 0.f;
+    if constexpr (decltype(MASK)::value) mask_unit(u + 1, sn);
 #pragma unroll
     for (int k = 0; k < NE; ++k) {
       if (k + PD < NE) vf[k + PD] = vread(slc, k + PD);
       if (k == 0) {
-        if constexpr (decltype(MASK)::value) mask_unit(u + 1, sn);
         mx = sn[0][0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sn[0][v]);
+        keep(mx);
+      }
+      if (k == 1) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sn[1][v]);
         mx = half_max(mx);
         keep(mx);
+        if constexpr (NE == 2) {
+          rf.alpha = newref(mx, rf.raise, rf.mref);
+          keep(rf.alpha);
+          keep(rf.mref);
+        }
       }
-      if (k == 1) {
+      if (NE > 2 && k == 2) {
         rf.alpha = newref(mx, rf.raise, rf.mref);
         keep(rf.alpha);
         keep(rf.mref);

@@ -17,6 +17,7 @@ from __future__ import annotations
 
 # MI355X (gfx950) published dense peaks.
 MFMA_BF16_TFLOPS = 2516.6          # 256 CUs x 4096 flop/clk/CU x 2.4 GHz
+MFMA_FP8_TFLOPS = 5033.2           # 256 CUs x 8192 flop/clk/CU x 2.4 GHz (dense)
 HBM_GBPS = 8000.0
 
 
@@ -43,3 +44,11 @@ def bwd_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elt_bytes: int) -> floa
 def decode_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, elt_bytes: int) -> float:
     """Compulsory split-KV traffic: K, V (Nk rows) and Q read once, O and fp32 LSE written once."""
     return 2.0 * B * Hkv * Nk * d * elt_bytes + 2.0 * B * Hq * Nq * d * elt_bytes + 4.0 * B * Hq * Nq
+
+
+def fp8_quant_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, elt_bytes: int, block_q: int, block_kv: int) -> float:
+    """Compulsory traffic of quantising Q, K and V: each input read once, one code byte per
+    element and one fp32 scale per block written (value tiles padded to 64 keys)."""
+    nkb = -(-N // 64) * 64
+    return ((B * Hq + 2.0 * B * Hkv) * N * d * elt_bytes + (B * Hq + B * Hkv) * N * d + B * Hkv * nkb * d
+            + 4.0 * (B * Hq * -(-N // block_q) + 2 * B * Hkv * -(-N // block_kv)))

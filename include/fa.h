@@ -167,8 +167,8 @@ fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, 
  * "Flash Attention" (wiki), section "FlashAttention-3": block quantization plus a
  * transform of random signs and a Hadamard matrix applied to queries and keys (the
  * same orthogonal transform on both leaves Q K^T unchanged in exact arithmetic and
- * spreads outliers over all coordinates); the explainer "What Hopper bought
- * FlashAttention-3": accuracy kept by per-block scaling.  Two steps: quantise Q and K
+ * spreads outliers over all coordinates); "FlashAttention" (explainer), section
+ * "What Hopper bought FlashAttention-3": accuracy kept by per-block scaling.  Two steps: quantise Q and K
  * (with the transform) and V once, then run the forward pass on the codes.
  *
  * Quantisation.  x [B,H,N,d] of `dtype` (16-byte aligned); signs: d floats of +1/-1

@@ -12,8 +12,8 @@ Sources (page title, then the part of the page):
 * "FlashAttention Primer: IO-Aware Attention, from FA1 to FA4", section
   "FlashAttention-3: Hopper asynchrony and FP8": scores are quantized in blocks and
   a random rotation is applied before quantization.
-* "What Hopper bought FlashAttention-3" (explainer): accuracy of the FP8 path is
-  kept by per-block scaling.
+* "FlashAttention" (explainer), section "What Hopper bought FlashAttention-3":
+  accuracy of the FP8 path is kept by per-block scaling.
 * Attention itself is :func:`oracle.attention.attention_fwd` on the dequantised
   operands.
 
