@@ -1,0 +1,205 @@
+"""Pins of the mask-family oracle (oracle/masks.py) to facts outside itself.
+
+* No mask and the causal window reduce to the square forward oracle (pinned in
+  test_oracle_pins.py); queries shorter than keys under the causal window reduce to the
+  split-KV oracle's bottom-right alignment (pinned in test_oracle_decode_pins.py); longer
+  queries leave the first Nq - Nk rows empty and the rest equal the square causal case.
+* Packed batches equal their sequences run one at a time through that oracle.
+* Closed form: with K = 0 every visible score is 0, so O_i is the mean of V over the
+  visible keys and LSE_i = ln(count_i), the count taken from the window's interval
+  arithmetic written out per row.
+* Dropping a tile from a block list equals deleting its keys; listing every tile equals
+  no list; an empty list (or no keys) gives O = 0 and LSE = -inf.
+* A scalar brute force (math.exp, math.fsum) over a packed batch with a window and
+  block lists.
+* Pair counts: N(N+1)/2 for the square causal case, and the window's closed form.
+Each planted mistake in MUTANTS must fail at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.decode as odec
+import oracle.masks as omasks
+from workloads import randn
+
+
+def _fixed(seed, B=1, Hq=4, Hkv=2, Nq=70, Nk=70, d=8):
+    return (randn(seed, (B, Hq, Nq, d), torch.float32).double().numpy(),
+            randn(seed + 1, (B, Hkv, Nk, d), torch.float32).double().numpy(),
+            randn(seed + 2, (B, Hkv, Nk, d), torch.float32).double().numpy())
+
+
+def pin_reduces_to_square_oracle(mod):
+    q, k, v = _fixed(1)
+    for window, causal in (((-1, -1), False), ((-1, 0), True)):
+        O, L = mod.attention_fwd_masked(q, k, v, 0.3, window=window)
+        O2, L2 = oracle.attention_fwd(q, k, v, causal, 0.3)
+        assert np.allclose(O, O2, atol=1e-13, rtol=0) and np.allclose(L, L2, atol=1e-13, rtol=0)
+
+
+def pin_short_queries_bottom_right(mod):
+    q, k, v = _fixed(2, Nq=9, Nk=130)
+    for window, causal in (((-1, 0), True), ((-1, -1), False)):
+        O, L = mod.attention_fwd_masked(q, k, v, 0.4, window=window)
+        O2, L2 = odec.attention_fwd_kv(q, k, v, causal, 0.4)
+        assert np.allclose(O, O2, atol=1e-13, rtol=0) and np.allclose(L, L2, atol=1e-13, rtol=0)
+
+
+def pin_long_queries(mod):
+    q, k, v = _fixed(3, Nq=50, Nk=20)
+    O, L = mod.attention_fwd_masked(q, k, v, 0.4, window=(-1, 0))
+    assert np.all(O[:, :, :30] == 0) and np.all(L[:, :, :30] == -np.inf)
+    O2, L2 = oracle.attention_fwd(q[:, :, 30:], k, v, True, 0.4)
+    assert np.allclose(O[:, :, 30:], O2, atol=1e-13, rtol=0) and np.allclose(L[:, :, 30:], L2, atol=1e-13, rtol=0)
+
+
+def _packed(seed, lq, lk, Hq=4, Hkv=2, d=8):
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = randn(seed, (Hq, cq[-1], d), torch.float32).double().numpy()
+    k = randn(seed + 1, (Hkv, ck[-1], d), torch.float32).double().numpy()
+    v = randn(seed + 2, (Hkv, ck[-1], d), torch.float32).double().numpy()
+    return q, k, v, cq, ck
+
+
+def pin_packed_is_per_sequence(mod):
+    lq, lk = [5, 40, 1, 33], [5, 70, 30, 33]
+    q, k, v, cq, ck = _packed(4, lq, lk)
+    for causal in (False, True):
+        O, L = mod.attention_fwd_masked(q, k, v, 0.35, cq, ck, window=(-1, 0) if causal else (-1, -1))
+        for b in range(4):
+            sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+            O2, L2 = odec.attention_fwd_kv(q[None, :, sq], k[None, :, sk], v[None, :, sk], causal, 0.35)
+            assert np.allclose(O[:, sq], O2[0], atol=1e-13, rtol=0)
+            assert np.allclose(L[:, sq], L2[0], atol=1e-13, rtol=0)
+
+
+def pin_window_closed_form(mod):
+    Nq, Nk = 40, 55
+    q, _, v = _fixed(5, Nq=Nq, Nk=Nk)
+    k = np.zeros((1, 2, Nk, 8))
+    for left, right in ((5, 0), (0, 0), (3, 7), (-1, 2), (12, -1)):
+        O, L = mod.attention_fwd_masked(q, k, v, 0.5, window=(left, right))
+        for i in range(Nq):
+            p = i + Nk - Nq
+            lo = 0 if left < 0 else max(0, p - left)
+            hi = Nk - 1 if right < 0 else min(Nk - 1, p + right)
+            cnt = hi - lo + 1
+            if cnt <= 0:
+                assert np.all(O[0, :, i] == 0) and np.all(L[0, :, i] == -np.inf)
+                continue
+            assert np.allclose(L[0, :, i], math.log(cnt), atol=1e-13, rtol=0)
+            ref = v[0, :, lo:hi + 1].mean(axis=1)                       # [Hkv, d]
+            assert np.allclose(O[0, :, i], np.repeat(ref, 2, axis=0), atol=1e-13, rtol=0)
+
+
+def pin_block_lists(mod):
+    Nq, Nk = 300, 200                      # query blocks of 256: 2; key tiles of 64: 4
+    q, k, v = _fixed(6, Hq=2, Hkv=1, Nq=Nq, Nk=Nk)
+    every = [[[[0, 1, 2, 3], [0, 1, 2, 3]]]]          # [B][Hm][query block] -> tiles
+    O, L = mod.attention_fwd_masked(q, k, v, 0.3, block_lists=every)
+    O2, L2 = mod.attention_fwd_masked(q, k, v, 0.3)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+    # drop tile 1 for query block 0 = delete keys 64..127 for queries 0..255
+    lists = [[[[0, 2, 3], [0, 1, 2, 3]]]]
+    O, L = mod.attention_fwd_masked(q, k, v, 0.3, block_lists=lists)
+    keep = np.r_[0:64, 128:200]
+    O3, L3 = odec.attention_fwd_kv(q[:, :, :256], k[:, :, keep], v[:, :, keep], False, 0.3)
+    assert np.allclose(O[:, :, :256], O3, atol=1e-13, rtol=0) and np.allclose(L[:, :, :256], L3, atol=1e-13, rtol=0)
+    assert np.allclose(O[:, :, 256:], O2[:, :, 256:], atol=1e-13, rtol=0)
+    # per-head lists, and an empty list -> zero rows with LSE = -inf
+    q2, k2, v2 = _fixed(7, B=2, Hq=2, Hkv=1, Nq=Nq, Nk=Nk)
+    lists = [[[[0, 1, 2, 3], []], [[], [3]]], [[[1], [0, 3]], [[2], [2]]]]
+    O, L = mod.attention_fwd_masked(q2, k2, v2, 0.3, block_lists=lists)
+    assert np.all(O[0, 0, 256:] == 0) and np.all(L[0, 0, 256:] == -np.inf)
+    assert np.all(O[0, 1, :256] == 0) and np.all(L[0, 1, :256] == -np.inf)
+    O4, L4 = odec.attention_fwd_kv(q2[1:, 1:, 256:], k2[1:, :, 128:192], v2[1:, :, 128:192], False, 0.3)
+    assert np.allclose(O[1, 1, 256:], O4[0, 0], atol=1e-13, rtol=0) and np.allclose(L[1, 1, 256:], L4[0, 0], atol=1e-13)
+
+
+def pin_empty_sequences(mod):
+    q, k, v, cq, ck = _packed(8, [3, 4, 0], [0, 6, 5])
+    O, L = mod.attention_fwd_masked(q, k, v, 0.3, cq, ck)
+    assert np.all(O[:, 0:3] == 0) and np.all(L[:, 0:3] == -np.inf)
+    assert np.all(np.isfinite(L[:, 3:7]))
+
+
+def pin_scalar_brute_force(mod):
+    lq, lk = [7, 3, 9], [7, 12, 4]
+    q, k, v, cq, ck = _packed(9, lq, lk, Hq=2, Hkv=1, d=3)
+    window = (2, 1)
+    lists = [[[[0]]], [[[0]]], [[[0]]]]                 # per sequence: one list for all heads, tile 0
+    O, L = mod.attention_fwd_masked(q, k, v, 0.7, cq, ck, window=window, block_lists=lists)
+    for b in range(3):
+        for h in range(2):
+            for i in range(lq[b]):
+                p = i + lk[b] - lq[b]
+                js = [j for j in range(lk[b]) if p - 2 <= j <= p + 1]
+                if not js:
+                    assert L[h, cq[b] + i] == -np.inf
+                    continue
+                s = [0.7 * math.fsum(q[h, cq[b] + i, c] * k[0, ck[b] + j, c] for c in range(3)) for j in js]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = math.fsum(e)
+                assert abs(L[h, cq[b] + i] - (mx + math.log(tot))) < 1e-13
+                for c in range(3):
+                    ref = math.fsum(e[t] * v[0, ck[b] + j, c] for t, j in enumerate(js)) / tot
+                    assert abs(O[h, cq[b] + i, c] - ref) < 1e-13
+
+
+def pin_pair_counts(mod):
+    assert mod.visible_pairs([100], [100], (-1, 0)) == 100 * 101 // 2
+    # causal window of w keys (left = w - 1): rows i >= w - 1 see w keys, earlier rows i + 1
+    w, n = 16, 100
+    assert mod.visible_pairs([n], [n], (w - 1, 0)) == sum(min(i + 1, w) for i in range(n))
+    assert mod.visible_pairs([5, 300], [9, 300], (-1, -1)) == 45 + 90000
+
+
+PINS = [pin_reduces_to_square_oracle, pin_short_queries_bottom_right, pin_long_queries, pin_packed_is_per_sequence,
+        pin_window_closed_form, pin_block_lists, pin_empty_sequences, pin_scalar_brute_force, pin_pair_counts]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_masks_oracle_pins(pin):
+    pin(omasks)
+
+
+MUTANTS = {
+    "top_left_alignment": ("p = i + (Lk - Lq)", "p = i"),
+    "window_left_off_by_one": ("vis &= j >= p - left", "vis &= j > p - left"),
+    "window_right_off_by_one": ("vis &= j <= p + right", "vis &= j < p + right"),
+    "query_block_128": ("vis &= tile_ok[i // QBLOCK,", "vis &= tile_ok[i // 128,"),
+    "empty_row_lse_zero": ("L = np.full(Lq, -np.inf)", "L = np.zeros(Lq)"),
+    "packed_keys_from_query_offsets": ("K[h // G, ks:ke], V[h // G, ks:ke]", "K[h // G, qs:qe], V[h // G, qs:qe]"),
+    "gqa_modulo": ("_attend(Q[b, h, r], K[b, h // G], V[b, h // G]", "_attend(Q[b, h, r], K[b, h % Hkv], V[b, h % Hkv]"),
+    "block_list_first_head_always": ("kl = hm[0] if len(hm) == 1 else hm[h]", "kl = hm[0]"),
+}
+
+
+def _mutant(old, new):
+    src = open(omasks.__file__).read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("oracle.masks_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "oracle_masks_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_masks_pins_catch_planted_mistake(name):
+    mod = _mutant(*MUTANTS[name])
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in PINS:
+            try:
+                pin(mod)
+            except (AssertionError, ValueError, IndexError, FloatingPointError):
+                failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"

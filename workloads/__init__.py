@@ -213,3 +213,87 @@ def make_fp8_inputs(w: Fp8Workload, N: int | None = None):
     f, m = w.outlier_frac, w.outlier_mult
     return (randn_outliers(w.seeds[0], (w.B, w.Hq, N, w.d), f, m), randn_outliers(w.seeds[1], (w.B, w.Hkv, N, w.d), f, m),
             randn_outliers(w.seeds[2], (w.B, w.Hkv, N, w.d), f, m), random_signs(w.seeds[3], w.d))
+
+
+@dataclass(frozen=True)
+class MaskWorkload:
+    """Forward attention under the mask family (bf16)."""
+    name: str
+    Hq: int
+    Hkv: int
+    d: int
+    seqlens_q: tuple          # per sequence
+    seqlens_k: tuple
+    packed: bool              # cumulative-length layout [H, total, d] (else [B, H, N, d])
+    window: tuple             # (left, right), -1 = unbounded
+    block: str = ""           # "" or the name of a block-list pattern
+    seeds: tuple = (0, 1, 2)
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def B(self) -> int:
+        return len(self.seqlens_q)
+
+
+def random_seqlens(seed: int, n: int, lo: int, hi: int) -> tuple:
+    """n lengths drawn uniformly from [lo, hi] by PCG64(seed)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return tuple(int(x) for x in g.integers(lo, hi + 1, size=n))
+
+
+def local_global_tiles(Lq: int, Lk: int, band: int = 8, stride: int = 16) -> list:
+    """Block list of one sequence and head: for each 256-query block, the 64-key tiles
+    within `band` tiles of the block's own diagonal tiles, plus every `stride`-th tile
+    (a local band with strided global columns)."""
+    nqb, nkt = -(-Lq // 256), -(-Lk // 64)
+    off = (Lk - Lq) // 64
+    out = []
+    for qb in range(nqb):
+        diag = range(4 * qb + off, 4 * qb + off + 4)
+        keep = sorted({t for t in range(nkt) if any(abs(t - c) < band for c in diag) or t % stride == 0})
+        out.append(keep)
+    return out
+
+
+MASK_WORKLOADS = {
+    "swa_b2_hq32_hkv8_n8192_d128_bf16_w1024": MaskWorkload(
+        "swa_b2_hq32_hkv8_n8192_d128_bf16_w1024", 32, 8, 128, (8192, 8192), (8192, 8192), False, (1023, 0),
+        seeds=(9700, 9701, 9702), note="causal sliding window of 1024 keys on the grouped-query N=8192 shape"),
+    "varlen_b8_hq32_hkv8_d128_bf16_causal": MaskWorkload(
+        "varlen_b8_hq32_hkv8_d128_bf16_causal", 32, 8, 128, random_seqlens(9710, 8, 256, 4096),
+        random_seqlens(9710, 8, 256, 4096), True, (-1, 0), seeds=(9711, 9712, 9713),
+        note="eight packed causal sequences of 256-4096 tokens"),
+    "bsparse_b1_hq16_hkv4_n8192_d128_bf16": MaskWorkload(
+        "bsparse_b1_hq16_hkv4_n8192_d128_bf16", 16, 4, 128, (8192,), (8192,), False, (-1, -1), "local_global",
+        seeds=(9720, 9721, 9722), note="block-sparse: a local band of 8 tiles around the diagonal plus every 16th tile"),
+    "mix_small_d64_bf16": MaskWorkload(
+        "mix_small_d64_bf16", 4, 2, 64, (300, 1, 77, 513), (600, 64, 77, 200), True, (100, 3), "local_global",
+        seeds=(9730, 9731, 9732), note="packed, unequal lengths, a two-sided window and block lists"),
+}
+MASK_HEADLINE = "swa_b2_hq32_hkv8_n8192_d128_bf16_w1024"
+
+
+def make_mask_inputs(w: MaskWorkload, dtype=torch.bfloat16):
+    """CPU tensors q, k, v (packed [H, total, d] or [B, H, N, d]), the cumulative lengths
+    (or None) and the block lists ([B][1][query block] -> tiles, or None)."""
+    if w.packed:
+        tq, tk = sum(w.seqlens_q), sum(w.seqlens_k)
+        q = randn(w.seeds[0], (w.Hq, tq, w.d), dtype)
+        k = randn(w.seeds[1], (w.Hkv, tk, w.d), dtype)
+        v = randn(w.seeds[2], (w.Hkv, tk, w.d), dtype)
+        cq = np.concatenate([[0], np.cumsum(w.seqlens_q)]).astype(np.int32)
+        ck = np.concatenate([[0], np.cumsum(w.seqlens_k)]).astype(np.int32)
+    else:
+        B, Nq, Nk = w.B, w.seqlens_q[0], w.seqlens_k[0]
+        q = randn(w.seeds[0], (B, w.Hq, Nq, w.d), dtype)
+        k = randn(w.seeds[1], (B, w.Hkv, Nk, w.d), dtype)
+        v = randn(w.seeds[2], (B, w.Hkv, Nk, w.d), dtype)
+        cq = ck = None
+    lists = None
+    if w.block == "local_global":
+        lists = [[local_global_tiles(lq, lk)] for lq, lk in zip(w.seqlens_q, w.seqlens_k)]
+    return q, k, v, cq, ck, lists
