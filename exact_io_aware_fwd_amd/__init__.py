@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     FA_F16,
     FA_OK,
     FaError,
+    block_lists_to_tensors,
     bwd,
     bwd_workspace_size,
     declared_symbols,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     fp8_quantize_v,
     fwd,
     fwd_fp8,
+    fwd_masked,
     fwd_splitkv,
     last_error,
     lse_combine,

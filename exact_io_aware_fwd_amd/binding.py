@@ -59,6 +59,9 @@ def load() -> ctypes.CDLL:
     L.fa_fwd_splitkv_num_splits.restype = _i64
     L.fa_lse_combine.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _vp]
     L.fa_lse_combine.restype = ctypes.c_int
+    L.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp]
+    L.fa_fwd_masked.restype = ctypes.c_int
     L.fa_fp8_v_codes_bytes.argtypes = [_i64, _i64, _i64, _i64]
     L.fa_fp8_v_codes_bytes.restype = ctypes.c_size_t
     L.fa_fp8_quantize_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _i64, _vp]
@@ -344,3 +347,85 @@ def fp8_prepare(q, k, v, signs=None, block_q: int = 64, block_kv: int = 64):
     k8, ks = fp8_quantize(k, block_kv, signs)
     v8, vs = fp8_quantize_v(v, block_kv)
     return q8, k8, v8, qs, ks, vs
+
+
+def block_lists_to_tensors(lists, maxq: int, maxk: int, device):
+    """Nested block lists [B][Hm][query block] -> key tiles into (block_cnt, block_idx)
+    int32 tensors of shapes [B, Hm, ceil(maxq/256)] and [B, Hm, ceil(maxq/256), ceil(maxk/64)]."""
+    B, Hm = len(lists), len(lists[0])
+    nqb, cap = -(-maxq // 256), -(-maxk // 64)
+    cnt = torch.zeros((B, Hm, nqb), dtype=torch.int32)
+    idx = torch.zeros((B, Hm, nqb, max(cap, 1)), dtype=torch.int32)
+    for b in range(B):
+        if len(lists[b]) != Hm:
+            raise ValueError("every sequence needs the same number of head lists")
+        for h in range(Hm):
+            for qb, tiles in enumerate(lists[b][h][:nqb]):
+                t = sorted(int(x) for x in tiles)[:cap]
+                cnt[b, h, qb] = len(t)
+                if t:
+                    idx[b, h, qb, :len(t)] = torch.tensor(t, dtype=torch.int32)
+    return cnt.to(device), idx.to(device)
+
+
+def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
+               max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, block_cnt=None, block_idx=None,
+               out=None, lse=None):
+    """O, LSE under the mask family via fa_fwd_masked.
+
+    Fixed lengths: q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d].  Packed: q [Hq,Nq,d], k/v [Hkv,Nk,d]
+    with cu_seqlens_q/k int32 [B+1] GPU tensors (max_seqlen_* default to Nq, Nk).
+    window = (left, right), -1 unbounded; (-1, 0) is causal (bottom-right aligned).
+    block_cnt/block_idx: int32 GPU tensors from block_lists_to_tensors, or None.
+    """
+    L = load()
+    packed = cu_seqlens_q is not None
+    dev = q.device
+    if packed:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+            raise ValueError("packed q, k, v must be [H, total, d] with k.shape == v.shape")
+        Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[0], k.shape[1]
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k is None or cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_k must have B+1 entries like cu_seqlens_q")
+        for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+            _check(t, n, dev, torch.int32)
+        mq = Nq if max_seqlen_q is None else int(max_seqlen_q)
+        mk = Nk if max_seqlen_k is None else int(max_seqlen_k)
+        lse_shape = (Hq, Nq)
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+            raise ValueError("q, k, v must be [B, H, N, d] with k.shape == v.shape")
+        B, Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("k, v must be [B, Hkv, Nk, d] matching q")
+        mq, mk = Nq, Nk
+        lse_shape = (B, Hq, Nq)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dev, q.dtype)
+    bh = 1
+    if block_idx is not None:
+        _check(block_cnt, "block_cnt", dev, torch.int32)
+        _check(block_idx, "block_idx", dev, torch.int32)
+        bh = block_idx.shape[1]
+        if block_cnt.shape != (B, bh, -(-mq // 256)) or block_idx.shape[:3] != block_cnt.shape or \
+                block_idx.shape[3] < -(-mk // 64):
+            raise ValueError("block_cnt / block_idx have the wrong shape")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
+    _check(o, "out", dev, q.dtype)
+    _check(lse_t, "lse", dev, torch.float32)
+    if o.shape != q.shape or tuple(lse_t.shape) != lse_shape:
+        raise ValueError("out/lse have the wrong shape")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, Hq, Hkv,
+                             Nq, Nk, d, _dtype_code(q), ptr(cu_seqlens_q), ptr(cu_seqlens_k), mq, mk,
+                             int(window[0]), int(window[1]), ptr(block_cnt), ptr(block_idx), bh, scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return o, lse_t

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -339,6 +340,71 @@ fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, 
   const hipError_t err = fa::launch_lse_combine(o_parts, lse_parts, o, lse, (long long)rows, (int)num_parts, (int)d,
                                                 dtype == FA_BF16, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "combine launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                        int64_t window_left, int64_t window_right, const int32_t* block_cnt,
+                        const int32_t* block_idx, int64_t block_heads, float softmax_scale,
+                        struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  const bool packed = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (packed && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr))
+    return fail(FA_ERR_INVALID_ARGUMENT, "give both cu_seqlens_q and cu_seqlens_k, or neither");
+  if (Nk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "Nk must be >= 0 (Nk=%lld)", (long long)Nk);
+  bool empty = false;
+  fa_status st = check_sizes(B, Hq, Hkv, std::max(Nq, Nk), d, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  const int64_t maxq = packed ? max_seqlen_q : Nq, maxk = packed ? max_seqlen_k : Nk;
+  if (packed && (max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > Nq || max_seqlen_k > Nk))
+    return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen_q/k must be in [0, Nq] / [0, Nk] (got %lld, %lld)",
+                (long long)max_seqlen_q, (long long)max_seqlen_k);
+  if (window_left < -1 || window_right < -1 || window_left > INT_MAX / 2 || window_right > INT_MAX / 2)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be -1 (unbounded) or >= 0 (got %lld, %lld)",
+                (long long)window_left, (long long)window_right);
+  if ((block_cnt == nullptr) != (block_idx == nullptr))
+    return fail(FA_ERR_INVALID_ARGUMENT, "give both block_cnt and block_idx, or neither");
+  if (block_idx != nullptr && block_heads != 1 && block_heads != Hq)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_heads must be 1 or Hq (got %lld)", (long long)block_heads);
+  if (B == 0 || maxq == 0 || Hq == 0) return FA_OK;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK)
+    return st;
+  if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK)) return st;
+  if (packed && ((st = check_ptr4(cu_seqlens_q, "cu_seqlens_q")) != FA_OK ||
+                 (st = check_ptr4(cu_seqlens_k, "cu_seqlens_k")) != FA_OK))
+    return st;
+  if (block_idx != nullptr && ((st = check_ptr4(block_cnt, "block_cnt")) != FA_OK ||
+                               (st = check_ptr4(block_idx, "block_idx")) != FA_OK))
+    return st;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.N = (int)Nq;
+  a.Nk = (int)Nk;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.maxq = (int)maxq;
+  a.maxk = (int)maxk;
+  a.wl = (int)window_left;
+  a.wr = (int)window_right;
+  a.bcnt = block_cnt;
+  a.bidx = block_idx;
+  a.bheads = block_idx ? (int)block_heads : 1;
+  a.bnq = (int)((maxq + 255) / 256);
+  a.bcap = (int)((maxk + 63) / 64);
+  const hipError_t err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "masked forward launch failed: %s", hipGetErrorString(err));
   return FA_OK;
 }
 

@@ -50,7 +50,21 @@
 
 namespace fa {
 
-template <class Tag, int D, bool CAUSAL>
+// Smallest p in [0, n) with list[p] >= t (n if none); list ascending.
+static __device__ __forceinline__ int lower_bound_tiles(const int* list, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < t) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// GEN = the mask family: per-sequence lengths (packed or fixed, queries and keys of
+// different lengths, bottom-right aligned), a window (left, right) and optional
+// block lists of key tiles; CAUSAL is then unused (causal is the window (-1, 0)).
+template <class Tag, int D, bool CAUSAL, bool GEN = false>
 __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
   constexpr int NW = 8;                 // waves per workgroup
@@ -86,21 +100,40 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   const int N = a.N;
 
   int b, hq, iq;
-  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  map_q_block(((GEN ? a.maxq : N) + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
   const int hkv = hq / (a.Hq / a.Hkv);
-  const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  // sequence geometry: Lq queries, Lk keys; first row of this head's sequence
+  int Lq = N, Lk = N;
+  size_t qhead, kvhead;
+  if constexpr (GEN) {
+    if (a.cu_q != nullptr) {   // packed; offsets clamped to the tensors whatever the lengths say
+      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
+      const int ks = min(max(a.cu_k[b], 0), a.Nk), ke = min(max(a.cu_k[b + 1], ks), a.Nk);
+      Lq = min(qe - qs, a.maxq);
+      Lk = min(ke - ks, a.maxk);
+      qhead = (size_t)hq * (size_t)N + qs;
+      kvhead = (size_t)hkv * (size_t)a.Nk + ks;
+    } else {
+      Lk = a.Nk;
+      qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+      kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+    }
+  } else {
+    qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+    kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  }
   const unsigned char* Qg = (const unsigned char*)a.q + qhead * ROWB;
   const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
   const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
 
   const int q0 = iq * BR;
+  if (GEN && q0 >= Lq) return;   // the whole workgroup: past this sequence's queries
   const int qw = q0 + wave * 32;   // first row of this wave
   const int myq = qw + r32;        // the query this lane's scores belong to
 
   // Q^T as the B operand: lane holds Q[myq][16s + 8hh .. +7]
   u32x4 qf[NS];
-  if (myq < N) {
+  if (myq < Lq) {
     const unsigned char* qp = Qg + (size_t)myq * ROWB + 16 * hh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qp + 32 * s);
@@ -109,14 +142,64 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     for (int s = 0; s < NS; ++s) qf[s] = u32x4{0, 0, 0, 0};
   }
 
-  const int nkv = (N + BC - 1) / BC;
-  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+  const int nkv = (Lk + BC - 1) / BC;
+  // Key tiles visited, in order: tile_of(j), j < ntile.  The mask family visits the tiles
+  // of the workgroup's key interval [klo, khi] (union over its queries of each query's
+  // window), filtered by the block list when there is one.
+  const int off = Lk - Lq;                  // query i sits at key position i + off
+  const int qlast = min(q0 + BR, Lq) - 1;
+  int ntile, t_lo = 0, p0 = 0;
+  const int* lst = nullptr;
+  int lo_q = 0, hi_q = Lk - 1;              // this lane's visible key interval
+  int JH = 0, JT = 0;                       // masked head [0, JH), plain [JH, JT), masked tail
+  if constexpr (GEN) {
+    auto lo_of = [&](int i) { return a.wl >= 0 ? i + off - a.wl : 0; };
+    auto hi_of = [&](int i) { return a.wr >= 0 ? min(i + off + a.wr, Lk - 1) : Lk - 1; };
+    lo_q = lo_of(myq);
+    hi_q = hi_of(myq);
+    const int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
+    t_lo = klo / BC;
+    const int t_hi = (Lk <= 0 || khi < klo) ? t_lo : khi / BC + 1;
+    // tiles that need element masks: below the largest lower bound, or past the smallest
+    // upper bound (which includes the tile holding key Lk-1 when Lk is ragged)
+    const int tm_head = (max(lo_of(qlast), 0) + BC - 1) / BC;     // tiles < tm_head
+    const int tm_tail = (hi_of(q0) + 1) / BC;                       // tiles >= tm_tail
+    int P1, P2;
+    if (a.bidx != nullptr) {
+      const int hm = a.bheads == 1 ? 0 : hq;
+      const size_t row = ((size_t)b * a.bheads + hm) * a.bnq + iq;
+      const int cnt = min(max(a.bcnt[row], 0), a.bcap);
+      lst = a.bidx + row * a.bcap;
+      p0 = lower_bound_tiles(lst, cnt, t_lo);
+      ntile = lower_bound_tiles(lst, cnt, t_hi) - p0;
+      P1 = lower_bound_tiles(lst, cnt, tm_head) - p0;
+      P2 = lower_bound_tiles(lst, cnt, tm_tail) - p0;
+    } else {
+      ntile = t_hi - t_lo;
+      P1 = tm_head - t_lo;
+      P2 = tm_tail - t_lo;
+    }
+    P1 = min(max(P1, 0), ntile);
+    P2 = min(max(P2, 0), ntile);
+    // tile j's mask flag covers its second unit and the next tile's first unit
+    JH = min(ntile, (P1 + 2) / 3 * 3);
+    JT = max(JH, max(P2 - 1, 0) / 3 * 3);
+  } else {
+    ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+  }
+  // tile index of list position j; past the list, the first tile past the keys (masked)
+  auto tile_of = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (!GEN) return j;
+    if (j >= ntile) return nkv;
+    if (lst == nullptr) return t_lo + j;
+    return min(max(lst[p0 + j], t_lo), nkv - 1);
+  };
 
   // ---- HBM -> LDS: tile t of K and V into slot sl ----
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
   auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
-    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+    Tiles::load(Kg, Vg, Lk, t, wave, doff, sl);
   };
 
   // ---- per-lane LDS offsets (plus immediates) ----
@@ -191,13 +274,17 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     u32x4 pf[2];   // P of the unit, packed B operands of the two 16-key steps
     u32x4 vpre[PD];  // first PD V fragments of the PV-phase
   };
+  // unit u's first key: half u % 2 of tile tile_of(u / 2)
   auto mask_unit = [&](int u, f32x16& s) __attribute__((always_inline)) {
-    const int k0 = u * 32;
-    int lim = N - k0 - 4 * hh;                           // key offset limit (exclusive)
-    if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+    const int k0 = GEN ? tile_of(u >> 1) * BC + 32 * (u & 1) : u * 32;
+    int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;   // key offset limit (exclusive)
+    if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+    const int llo = lo_q - k0 - 4 * hh;                       // first visible offset (GEN)
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (8 * (v >> 2) + (v & 3) >= lim) s[v] = -INFINITY;
+    for (int v = 0; v < 16; ++v) {
+      const int o = 8 * (v >> 2) + (v & 3);
+      if (o >= lim || (GEN && o < llo)) s[v] = -INFINITY;
+    }
   };
   auto sphase = [&](const unsigned char* slc, int hc, const unsigned char* sln, int hn, f32x16& sc,
                     f32x16& sn, const Ref& rf, Pend& pd) __attribute__((always_inline)) {
@@ -291,7 +378,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
       wait_loads();      // this wave's loads of tile j+1 landed
       __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
-    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    if (j + 2 < ntile) dma(tile_of(j + 2), slot((T + 2) % 3));
     if constexpr (!decltype(LATE)::value) sphase(sc, 0, sc, 1, sa, sb, rf, p0);
     pphase(MASK, 2 * j, sc, 0, sn, 0, sa, sb, rf, p0);
     sphase(sc, 1, sn, 0, sb, sa, rf, p1);
@@ -303,8 +390,9 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   using Plain = std::false_type;
   using Masked = std::true_type;
 
-  dma(0, slot0);
-  if (ntile > 1) dma(1, slot1);
+  if (!GEN || ntile > 0) {   // (a mask-family workgroup may have no tile to visit)
+  dma(tile_of(0), slot0);
+  if (ntile > 1) dma(tile_of(1), slot1);
   wait_loads();
   __syncthreads();
   sa = zero16();
@@ -316,11 +404,23 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   rf.alpha = newref(half_max(rowmax16(sa)), rf.raise, rf.mref);
   // Tiles whose units, and the unit after them, all precede every wave's last unit (the
   // one holding its diagonal when causal, or the last key) need no mask.
-  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
-  const int J1 = min(ntile, max(ulast0 - 1, 0) / 2) / 3 * 3;
+  if constexpr (!GEN) {
+    const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
+    JT = min(ntile, max(ulast0 - 1, 0) / 2) / 3 * 3;
+  }
   auto run = [&](auto LATE) __attribute__((always_inline)) {
     int j = 0;
-    for (; j < J1; j += 3) {
+    if constexpr (GEN) {
+      for (; j < JH; j += 3) {
+        tile(I0{}, Masked{}, LATE, j);
+        if (j + 1 >= ntile) break;
+        tile(I1{}, Masked{}, LATE, j + 1);
+        if (j + 2 >= ntile) break;
+        tile(I2{}, Masked{}, LATE, j + 2);
+      }
+      j = JH;
+    }
+    for (; j < JT; j += 3) {
       tile(I0{}, Plain{}, LATE, j);
       tile(I1{}, Plain{}, LATE, j + 1);
       tile(I2{}, Plain{}, LATE, j + 2);
@@ -335,11 +435,13 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   };
   if (wave >= NW / 2) run(std::true_type{});
   else run(std::false_type{});
+  }
 
-  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
+  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l); a row that saw no key (mask
+  // family only) gets O = 0 and LSE = -inf
   const float l_tot = half_sum(l_run);
-  if (myq < N) {
-    const float inv = 1.f / l_tot;
+  if (myq < Lq) {
+    const float inv = (GEN && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
     unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -350,7 +452,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
                          E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
         *(u32x2*)(Og + d0 * 2) = w;
       }
-    if (hh == 0) a.lse[qhead + myq] = (mr + log2f(l_tot)) * kLn2;
+    if (hh == 0) a.lse[qhead + myq] = (GEN && !(l_tot > 0.f)) ? -INFINITY : (mr + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -362,6 +464,21 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   if (nblocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
   return hipGetLastError();
+}
+
+template <class Tag, int D>
+static hipError_t launch_fwd_masked_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BR = 256;
+  const int nqb = (a.maxq + BR - 1) / BR;
+  const long long nblocks = (long long)a.B * a.Hq * nqb;
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_kernel<Tag, D, false, true>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_masked(const FwdArgs& a, int d, bool bf16, hipStream_t stream) {
+  if (bf16) return d == 128 ? launch_fwd_masked_t<bf16_tag, 128>(a, stream) : launch_fwd_masked_t<bf16_tag, 64>(a, stream);
+  return d == 128 ? launch_fwd_masked_t<f16_tag, 128>(a, stream) : launch_fwd_masked_t<f16_tag, 64>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream) {

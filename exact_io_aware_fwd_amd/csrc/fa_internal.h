@@ -16,6 +16,16 @@ struct FwdArgs {
   int B, Hq, Hkv, N;
   float scale;        // softmax scale
   float scale_log2;   // softmax scale * log2(e)
+  // Mask family (the general kernel only).  Fixed lengths: q [B,Hq,N,d], k/v [B,Hkv,Nk,d].
+  // Packed (cu_q != null): q [Hq,N,d], k/v [Hkv,Nk,d], sequence b = rows cu[b] .. cu[b+1]-1.
+  int Nk = 0;
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int maxq = 0, maxk = 0;     // longest sequence (grid size; rows past it are not computed)
+  int wl = -1, wr = -1;       // window (left, right), -1 = unbounded
+  const int* bcnt = nullptr;  // block lists: counts [B, bheads, bnq]
+  const int* bidx = nullptr;  //              tiles  [B, bheads, bnq, bcap], ascending
+  int bheads = 1, bnq = 0, bcap = 0;
 };
 
 struct BwdArgs {
@@ -109,10 +119,11 @@ struct Fp8FwdArgs {
 
 // Return a hipError_t from the launches (hipSuccess when all were enqueued).
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_fwd_masked(const FwdArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_splitkv(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
-hipError_t launch_fp8_quant(const QuantArgs& a, int d, bool bf16, int mode, hipStream_t stream);  // mode 0: rows
-                                                                                                 // + transform, 1: rows, 2: value tiles
+// mode 0: rows with the transform, 1: rows, 2: value tiles
+hipError_t launch_fp8_quant(const QuantArgs& a, int d, bool bf16, int mode, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, float* lse, long long rows, int S,
                               int d, bool bf16, hipStream_t stream);

@@ -162,6 +162,43 @@ fa_status fa_lse_combine(const float* o_parts, const float* lse_parts, void* o, 
                          struct ihipStream_t* stream);
 
 /*
+ * Forward pass under the mask family: variable-length (packed) batches, queries and
+ * keys of different lengths, sliding windows and block-sparse tile lists.
+ *
+ * "FlashAttention Primer" sections "FlashAttention-2: better work partitioning"
+ * (variable-length entry points, sliding-window attention) and "Hardware, dtype,
+ * determinism, and padding caveats" (cu_seqlens); "Flash Attention" (wiki) sections
+ * "Block-sparse FlashAttention" (masked blocks skipped, exact on the kept blocks) and
+ * "Specialized kernels have boundaries" (causal conventions for unequal lengths).
+ *
+ * Layout.  Fixed lengths (cu_seqlens_q == cu_seqlens_k == NULL): q, o [B,Hq,Nq,d],
+ * k, v [B,Hkv,Nk,d], lse [B,Hq,Nq].  Packed: q, o [Hq,Nq,d] and k, v [Hkv,Nk,d] with
+ * Nq, Nk the total rows, lse [Hq,Nq]; sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows likewise (int32, B+1 entries each,
+ * device memory, nondecreasing); max_seqlen_q / max_seqlen_k bound the sequence lengths
+ * (rows past them are not computed; offsets are clamped to the tensors, so inconsistent
+ * arrays give unspecified rows, not invalid accesses).  In fixed mode the max lengths
+ * are ignored.
+ * Masking.  Within a sequence of Lq queries and Lk keys, query i sits at key position
+ * p = i + Lk - Lq (bottom-right alignment).  Key j is visible iff
+ * (window_left < 0 or j >= p - window_left) and (window_right < 0 or j <= p + window_right);
+ * (-1, -1) is full attention and (-1, 0) causal.  With block lists, queries are cut into
+ * blocks of 256 and keys into tiles of 64; block_cnt [B, block_heads, ceil(maxq/256)] and
+ * block_idx [B, block_heads, ceil(maxq/256), ceil(maxk/64)] (int32, device; maxq, maxk =
+ * Nq, Nk in fixed mode) list, per (sequence, head or all heads, query block), the key
+ * tiles to visit in ascending order; other tiles are skipped (their scores masked).
+ * block_heads is 1 (one list for all heads) or Hq.  A query that sees no key gets O = 0
+ * and LSE = -inf.  softmax_scale, dtype and head sizes as in fa_fwd.  Deterministic;
+ * nothing is allocated.
+ */
+fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                        int64_t window_left, int64_t window_right, const int32_t* block_cnt,
+                        const int32_t* block_idx, int64_t block_heads, float softmax_scale,
+                        struct ihipStream_t* stream);
+
+/*
  * FP8 (e4m3) forward pass with per-block scales and incoherent processing.
  *
  * "Flash Attention" (wiki), section "FlashAttention-3": block quantization plus a

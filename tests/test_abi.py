@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
                           "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_num_splits",
                           "fa_lse_combine", "fa_fp8_v_codes_bytes", "fa_fp8_quantize_rows", "fa_fp8_quantize_v",
-                          "fa_fwd_fp8"}
+                          "fa_fwd_fp8", "fa_fwd_masked"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -211,3 +211,29 @@ def test_fwd_fp8_empty_and_sizes(L):
     assert L.fa_fp8_v_codes_bytes(2, 3, 100, 128) == 2 * 3 * 2 * 128 * 64
     assert L.fa_fp8_v_codes_bytes(1, 1, 64, 64) == 64 * 64
     assert L.fa_fp8_v_codes_bytes(1, 1, 0, 64) == 0
+
+
+def masked(L, B=1, Hq=2, Hkv=1, Nq=100, Nk=120, d=128, dtype=1, cq=None, ck=None, mq=0, mk=0, wl=-1, wr=-1,
+           bcnt=None, bidx=None, bh=1, scale=0.125, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse")}
+    p.update(ptrs)
+    return L.fa_fwd_masked(p["q"], p["k"], p["v"], p["o"], p["lse"], B, Hq, Hkv, Nq, Nk, d, dtype, cq, ck, mq, mk,
+                           wl, wr, bcnt, bidx, bh, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INV), (dict(lse=P + 4), INV), (dict(Nk=-1), INV), (dict(Hq=3, Hkv=2), INV), (dict(d=80), UNS),
+    (dict(cq=P), INV),                                      # one cu array without the other
+    (dict(cq=P, ck=P, mq=101, mk=10), INV),                 # max length beyond the tensor rows
+    (dict(cq=P + 2, ck=P, mq=10, mk=10), INV),              # misaligned
+    (dict(wl=-2), INV), (dict(wr=-5), INV), (dict(bcnt=P), INV), (dict(bcnt=P, bidx=P, bh=3), INV),
+    (dict(scale=float("nan")), INV),
+])
+def test_fwd_masked_rejects(L, kw, expect):
+    assert masked(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+def test_fwd_masked_empty(L):
+    assert masked(L, B=0) == OK and masked(L, Nq=0) == OK
+    assert masked(L, cq=P, ck=P, mq=0, mk=5) == OK        # every sequence empty
