@@ -14,6 +14,7 @@ of the same workload on the host cores.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--fwd-only]
     python bench.py --decode [--steps K] ...    # split-KV decoding: GB/s against the HBM peak
     python bench.py --fp8 [--steps K] ...       # FP8 forward (quantise + attention): TFLOP/s
+    python bench.py --masks [--steps K] ...     # mask-family forward (sliding window; varlen, block-sparse)
 
 Profiling helpers (rocprofv3 runs of this same script):
     python bench.py --copy-calibration          # a plain 1 GiB device copy, for HBM counters
@@ -57,6 +58,10 @@ def parse():
                         "(SUBSTR may list alternatives separated by '|')")
     p.add_argument("--decode", action="store_true",
                    help="time the split-KV decoding forward instead (one JSON line, GB/s)")
+    p.add_argument("--masks", action="store_true",
+                   help="time the mask-family forward (sliding window headline; varlen and block-sparse alongside)")
+    p.add_argument("--headline-only", action="store_true",
+                   help="with --masks: skip the workloads timed alongside (profiling runs)")
     p.add_argument("--fp8", action="store_true",
                    help="time the FP8 forward (block quantisation with the Hadamard transform + attention)")
     return p.parse_args()
@@ -69,6 +74,8 @@ KERNEL_SOURCES = {
             "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
     "decode": ["exact_io_aware_fwd_amd/csrc/fa_decode.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
                "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
+    "masks": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
+              "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
     "fp8": ["exact_io_aware_fwd_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
             "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
 }
@@ -141,7 +148,7 @@ def record_traffic(kdir, cdir, substr):
     fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
     write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
     kind = ("decode" if ("splitkv" in substr or "combine" in substr) else "fp8" if "fp8" in substr
-            else "bwd" if "bwd" in substr else "fwd")
+            else "masks" if "true>" in substr else "bwd" if "bwd" in substr else "fwd")
     data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
                   "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
@@ -355,6 +362,94 @@ def bench_fp8(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_masks(args):
+    """Mask-family forward: one JSON line for the N=8192 sliding-window workload in
+    TFLOP/s over the visible (query, key) pairs; the packed variable-length and the
+    block-sparse workloads are timed alongside (under `passes`)."""
+    import numpy as np
+    import torch
+    import workloads
+    import oracle.masks as om
+    import exact_io_aware_fwd_amd as fa
+    from exact_io_aware_fwd_amd import metrics
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prepare(w):
+        q, k, v, cq, ck, lists = workloads.make_mask_inputs(w)
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
+        if w.packed:
+            mq, mk = max(w.seqlens_q), max(w.seqlens_k)
+            cqd, ckd = torch.from_numpy(cq).to(dev), torch.from_numpy(ck).to(dev)
+        else:
+            mq, mk, cqd, ckd = w.seqlens_q[0], w.seqlens_k[0], None, None
+        bc, bi = fa.block_lists_to_tensors(lists, mq, mk, dev) if lists is not None else (None, None)
+        o, lse = torch.empty_like(qd), torch.empty(qd.shape[:-1], dtype=torch.float32, device=dev)
+        run = lambda: fa.fwd_masked(qd, kd, vd, w.window, w.scale, cqd, ckd, mq, mk, bc, bi, out=o, lse=lse)
+        pairs = sum(om.visible_pairs([lq], [lk], w.window, None if lists is None else [lists[b][0]])
+                    for b, (lq, lk) in enumerate(zip(w.seqlens_q, w.seqlens_k)))
+        flops = 4.0 * w.d * w.Hq * pairs
+        return run, flops, (q, k, v, cq, ck, lists)
+
+    def timed(run, steps):
+        for _ in range(max(args.warmup, 3)):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
+
+    w = workloads.MASK_WORKLOADS[args.workload or workloads.MASK_HEADLINE]
+    run, flops, cpu_inputs = prepare(w)
+    ms, wall_ms = timed(run, args.steps)
+    achieved = flops / (ms * 1e-3) / 1e12
+    passes = {}
+    for name in workloads.MASK_WORKLOADS:
+        if name == w.name or name.startswith("mix_") or args.headline_only:
+            continue
+        r2, f2, _ = prepare(workloads.MASK_WORKLOADS[name])
+        m2, _ = timed(r2, args.steps)
+        passes[name] = {"ms": m2, "TFLOPs": f2 / (m2 * 1e-3) / 1e12, "visible_pair_flops": f2}
+    rec = {
+        "metric": "mask-family attention forward TFLOPS (visible pairs) and % of the MFMA peak, sliding window at N=8192 d=128",
+        "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, 3),
+        "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded iid N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.seqlens_q[0], "Nk": w.seqlens_k[0],
+                   "d": w.d, "window": list(w.window), "step": "fa_fwd_masked",
+                   "flops": "4 d x visible (query, key) pairs x heads"},
+        "passes": passes,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": metrics.MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / metrics.MFMA_BF16_TFLOPS, "traffic": traffic_bytes("masks"),
+                     "kernel": "fwd_kernel<bf16, 128, false, true>", "avg_ms": ms, "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        q, k, v, cq, ck, lists = cpu_inputs
+        G = w.Hq // w.Hkv
+        heads = max(G, min(args.cpu_heads, w.Hq) // G * G)
+        t1 = time.perf_counter()
+        om.attention_fwd_masked(q[:1, :heads], k[:1, :heads // G], v[:1, :heads // G], w.scale, window=w.window)
+        dt = time.perf_counter() - t1
+        sflops = flops / (w.B * w.Hq) * heads
+        rec["cpu_baseline"] = {"value": sflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                               "sample": f"batch 0, query heads 0-{heads - 1} with their K/V heads, all rows, "
+                                         f"numpy float64 (materialising the full N x N scores and masking them; "
+                                         f"credited the visible-pair FLOPs); {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -372,6 +467,9 @@ def main():
         sys.exit(2)
     if args.fp8:
         bench_fp8(args)
+        return
+    if args.masks:
+        bench_masks(args)
         return
     if args.decode:
         bench_decode(args)
