@@ -19,10 +19,11 @@
 //    e4m3(value * 2^-e), round to nearest even (v_cvt_pk_fp8_f32).  Scaling by a power
 //    of two is exact, so every code is decided by one rounding of an fp32 value.
 //
-// gfx950 design.  One workgroup per scale block, four rows per thread and eight
-// consecutive columns per thread (one 16-byte load); the d/8 threads of a row are
-// adjacent lanes, so the butterfly stages across them are lane exchanges.  The values
-// stay in registers between the block maximum and the encoding (one HBM read).
+// gfx950 design.  One workgroup per scale block (block_rows * d / 64 threads), two rows
+// per thread and 32 consecutive columns per thread (four 16-byte loads); five butterfly
+// stages run inside the thread and the d/32 threads of a row are lanes of one quad, so
+// the remaining one or two stages are DPP quad permutations (no LDS traffic).  The
+// values stay in registers between the block maximum and the encoding (one HBM read).
 //  * Query/key codes keep the input layout [B, H, N, d].
 //  * Value codes are written in the layout the forward pass feeds to the matrix core:
 //    per 64-key tile a transposed [d][64] byte block, [B, H, ceil(N/64), d, 64], with
@@ -52,13 +53,24 @@ static __device__ __forceinline__ float pow2f(int e) {
   return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
+// Lane exchange within quads for the butterflies across threads: lane l receives the
+// value of lane l ^ M (M = 1 or 2), one DPP move per 32-bit half.
+template <int M>
+static __device__ __forceinline__ double quad_xor(double x) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 template <class Tag, int D, bool ROT, bool VT>
-__global__ void __launch_bounds__(1024) fp8_quant_kernel(const QuantArgs a) {
+__global__ void __launch_bounds__(512) fp8_quant_kernel(const QuantArgs a) {
   using E = Elt<Tag>;
-  constexpr int TPR = D / 8;         // threads per row
-  constexpr int NP = 4;              // rows per thread
+  constexpr int TPR = D / 32;        // threads per row (32 consecutive columns each)
+  constexpr int NP = 2;              // rows per thread
   const int t = threadIdx.x;
-  const int nt = blockDim.x;         // block_rows * D / 32
+  const int nt = blockDim.x;         // block_rows * D / 64
   const int rpp = nt / TPR;          // rows per pass
   const int j = t % TPR;
   const int r0 = t / TPR;
@@ -67,59 +79,69 @@ __global__ void __launch_bounds__(1024) fp8_quant_kernel(const QuantArgs a) {
   const int row0 = blk * a.block_rows;
   const uint16_t* X = (const uint16_t*)a.x + (size_t)bh * a.N * D;
 
-  float sg[8];
+  uint32_t negm = 0;                 // bit i: column 32j + i has sign -1
   if constexpr (ROT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sg[i] = a.signs[8 * j + i];
+    for (int i = 0; i < 32; ++i) negm |= (a.signs[32 * j + i] < 0.f ? 1u : 0u) << i;
   }
 
-  float y[NP][8];
+  float y[NP][32];
   float amax = 0.f;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = row0 + p * rpp + r0;
-    u32x4 raw = {0, 0, 0, 0};
-    if (row < a.N) raw = *(const u32x4*)(X + (size_t)row * D + 8 * j);
-    float f[8];
+    u32x4 raw[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (row < a.N) {
+      const u32x4* src = (const u32x4*)(X + (size_t)row * D + 32 * j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = E::to_f32((uint16_t)(raw[i] & 0xFFFFu));
-      f[2 * i + 1] = E::to_f32((uint16_t)(raw[i] >> 16));
+      for (int c = 0; c < 4; ++c) raw[c] = src[c];
     }
+    float f[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[8 * c + 2 * i] = E::to_f32((uint16_t)(raw[c][i] & 0xFFFFu));
+        f[8 * c + 2 * i + 1] = E::to_f32((uint16_t)(raw[c][i] >> 16));
+      }
     if constexpr (ROT) {
-      double z[8];
+      double z[32];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = (double)(f[i] * sg[i]);   // exact: sg is +-1
-      // butterflies over the three index bits inside the thread ...
+      for (int i = 0; i < 32; ++i) z[i] = (double)((negm >> i) & 1u ? -f[i] : f[i]);
+      // butterflies over the five index bits inside the thread ...
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
+      for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 32; ++i)
           if (!(i & h)) {
             const double u = z[i], w = z[i + h];
             z[i] = u + w;
             z[i + h] = u - w;
           }
-      // ... and over the index bits that select the thread (adjacent lanes)
+      // ... and over the bits that select the thread: the lower index keeps u + w, the
+      // upper gets u - w = o - z (o the partner's value); all sums are exact
+      if constexpr (TPR >= 2) {
+        const double s1 = (j & 1) ? -1.0 : 1.0;
 #pragma unroll
-      for (int m = 1; m < TPR; m <<= 1)
+        for (int i = 0; i < 32; ++i) z[i] = fma(s1, z[i], quad_xor<1>(z[i]));
+      }
+      if constexpr (TPR >= 4) {
+        const double s2 = (j & 2) ? -1.0 : 1.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const double o = __shfl_xor(z[i], m, 64);
-          z[i] = (j & m) ? o - z[i] : z[i] + o;
-        }
+        for (int i = 0; i < 32; ++i) z[i] = fma(s2, z[i], quad_xor<2>(z[i]));
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[p][i] = (float)(z[i] * a.inv_sqrt_d);
+      for (int i = 0; i < 32; ++i) y[p][i] = (float)(z[i] * a.inv_sqrt_d);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[p][i] = f[i];
+      for (int i = 0; i < 32; ++i) y[p][i] = f[i];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[p][i]));
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[p][i]));
   }
 
   // block maximum: lanes, then waves through LDS
-  __shared__ float red[16];
+  __shared__ float red[8];
   __shared__ int eblk;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
@@ -135,11 +157,11 @@ __global__ void __launch_bounds__(1024) fp8_quant_kernel(const QuantArgs a) {
   __syncthreads();
   const float inv = pow2f(-eblk);     // -e in [-127, 127]; e <= 126 for finite fp32 data
 
-  uint32_t code[NP][2];
+  uint32_t code[NP][8];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 8; ++h) {
       int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[p][4 * h] * inv, y[p][4 * h + 1] * inv, 0, false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(y[p][4 * h + 2] * inv, y[p][4 * h + 3] * inv, w, true);
       code[p][h] = (uint32_t)w;
@@ -149,18 +171,26 @@ __global__ void __launch_bounds__(1024) fp8_quant_kernel(const QuantArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int row = row0 + p * rpp + r0;
-      if (row < a.N) *(u32x2*)(a.codes + ((size_t)bh * a.N + row) * D + 8 * j) = u32x2{code[p][0], code[p][1]};
+      if (row < a.N) {
+        u32x4* dst = (u32x4*)(a.codes + ((size_t)bh * a.N + row) * D + 32 * j);
+        dst[0] = u32x4{code[p][0], code[p][1], code[p][2], code[p][3]};
+        dst[1] = u32x4{code[p][4], code[p][5], code[p][6], code[p][7]};
+      }
     }
   } else {
     // transpose through LDS: the block's codes as [row][d] bytes, then 16-byte segments
     // of the [d][64] tiles, each gathered from one column
     __shared__ __attribute__((aligned(16))) unsigned char tileb[256 * D];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) *(u32x2*)(tileb + (p * rpp + r0) * D + 8 * j) = u32x2{code[p][0], code[p][1]};
+    for (int p = 0; p < NP; ++p) {
+      u32x4* dst = (u32x4*)(tileb + (p * rpp + r0) * D + 32 * j);
+      dst[0] = u32x4{code[p][0], code[p][1], code[p][2], code[p][3]};
+      dst[1] = u32x4{code[p][4], code[p][5], code[p][6], code[p][7]};
+    }
     __syncthreads();
     const int nkb = (a.N + 63) / 64;
 #pragma unroll
-    for (int sgi = 0; sgi < 2; ++sgi) {
+    for (int sgi = 0; sgi < 4; ++sgi) {
       const int s = t + sgi * nt;           // segment: tile kt, row d, quarter qq
       const int kt = s / (4 * D);
       const int d = (s / 4) % D;
@@ -184,7 +214,7 @@ template <class Tag, int D>
 static hipError_t launch_quant_t(const QuantArgs& a, int mode, hipStream_t stream) {
   const long long nblocks = (long long)a.BH * a.nblk;
   if (nblocks <= 0) return hipSuccess;
-  const int nt = a.block_rows * D / 32;
+  const int nt = a.block_rows * D / 64;
   if (mode == 0) hipLaunchKernelGGL((fp8_quant_kernel<Tag, D, true, false>), dim3((unsigned)nblocks), dim3(nt), 0, stream, a);
   else if (mode == 1) hipLaunchKernelGGL((fp8_quant_kernel<Tag, D, false, false>), dim3((unsigned)nblocks), dim3(nt), 0, stream, a);
   else hipLaunchKernelGGL((fp8_quant_kernel<Tag, D, false, true>), dim3((unsigned)nblocks), dim3(nt), 0, stream, a);
