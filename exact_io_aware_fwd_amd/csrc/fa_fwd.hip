@@ -274,9 +274,19 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
     u32x4 pf[2];   // P of the unit, packed B operands of the two 16-key steps
     u32x4 vpre[PD];  // first PD V fragments of the PV-phase
   };
+  // Keys every query of this wave sees: [wlo, whi] (wave-uniform); a unit inside it needs
+  // no per-element mask.
+  int wlo = 0, whi;
+  if constexpr (GEN) {
+    wlo = a.wl >= 0 ? max(min(qw + 31, Lq - 1) + off - a.wl, 0) : 0;
+    whi = a.wr >= 0 ? min(qw + off + a.wr, Lk - 1) : Lk - 1;
+  } else {
+    whi = CAUSAL ? min(qw, N - 1) : N - 1;
+  }
   // unit u's first key: half u % 2 of tile tile_of(u / 2)
   auto mask_unit = [&](int u, f32x16& s) __attribute__((always_inline)) {
     const int k0 = GEN ? tile_of(u >> 1) * BC + 32 * (u & 1) : u * 32;
+    if (k0 >= wlo && k0 + 31 <= whi) return;
     int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;   // key offset limit (exclusive)
     if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
     const int llo = lo_q - k0 - 4 * hh;                       // first visible offset (GEN)
