@@ -33,6 +33,11 @@ Readings taken where the pages are silent (listed with the others in the design 
   into tiles of 64; for each (sequence, head or all heads, query block) the caller lists
   the key tiles to visit; a score outside the listed tiles is masked.
 * A query that sees no key gets O = 0 and LSE = -inf.
+* Gradients ("FlashAttention Primer", section "Backward pass: recomputation instead of
+  storage", with the full softmax Jacobian as in :mod:`oracle.attention`): for every
+  visible pair, P = exp(S - LSE), dV += P^T dO, dP = dO V^T, D_i = sum_k dO_ik O_ik,
+  dS = P * (dP - D), dQ = scale dS K, dK += scale dS^T Q; masked pairs and rows without
+  keys contribute nothing; dK and dV of a K/V head sum over its query heads.
 
 Pins: tests/test_oracle_masks_pins.py.
 """
@@ -143,3 +148,47 @@ def visible_pairs(Lqs, Lks, window=(-1, -1), block_lists_one_head=None) -> int:
         kl = None if block_lists_one_head is None else block_lists_one_head[b]
         n += int(visible(int(lq), int(lk), window, kl).sum())
     return n
+
+
+def attention_bwd_masked(q, k, v, do, scale: float, cu_seqlens_q=None, cu_seqlens_k=None, window=(-1, -1)):
+    """(dQ, dK, dV) in float64 of L(O) for O = attention_fwd_masked(q, k, v, ...) (no block
+    lists), with dO = dL/dO.  Layouts as in attention_fwd_masked."""
+    Q, K, V, dO = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    scale = float(scale)
+    O, LSE = attention_fwd_masked(Q, K, V, scale, cu_seqlens_q, cu_seqlens_k, window)
+    packed = cu_seqlens_q is not None
+    if packed:
+        cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+        ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+        B, Hq, Hkv = len(cq) - 1, Q.shape[0], K.shape[0]
+    else:
+        B, Hq, Nq, _ = Q.shape
+        Hkv, Nk = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for b in range(B):
+        for h in range(Hq):
+            if packed:
+                sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+                Qb, Kb, Vb, dOb, Ob, Lb = Q[h, sq], K[h // G, sk], V[h // G, sk], dO[h, sq], O[h, sq], LSE[h, sq]
+            else:
+                Qb, Kb, Vb, dOb, Ob, Lb = Q[b, h], K[b, h // G], V[b, h // G], dO[b, h], O[b, h], LSE[b, h]
+            vis = visible(Qb.shape[0], Kb.shape[0], window)
+            ok = np.isfinite(Lb)
+            S = scale * (Qb @ Kb.T)
+            P = np.where(vis & ok[:, None], np.exp(S - np.where(ok, Lb, 0.0)[:, None]), 0.0)
+            dVb = P.T @ dOb
+            dP = dOb @ Vb.T
+            Dr = (dOb * Ob).sum(axis=1)
+            dS = P * (dP - Dr[:, None])
+            dQb = scale * (dS @ Kb)
+            dKb = scale * (dS.T @ Qb)
+            if packed:
+                dQ[h, sq] = dQb
+                dK[h // G, sk] += dKb
+                dV[h // G, sk] += dVb
+            else:
+                dQ[b, h] = dQb
+                dK[b, h // G] += dKb
+                dV[b, h // G] += dVb
+    return dQ, dK, dV

@@ -162,8 +162,60 @@ def pin_pair_counts(mod):
     assert mod.visible_pairs([5, 300], [9, 300], (-1, -1)) == 45 + 90000
 
 
+def pin_bwd_reduces_to_square_oracle(mod):
+    q, k, v = _fixed(20, Hq=4, Hkv=2, Nq=40, Nk=40)
+    do = randn(23, q.shape, torch.float32).double().numpy()
+    for window, causal in (((-1, -1), False), ((-1, 0), True)):
+        g1 = mod.attention_bwd_masked(q, k, v, do, 0.3, window=window)
+        g2 = oracle.attention_bwd(q, k, v, do, causal, 0.3)
+        for a, b in zip(g1, g2):
+            assert np.allclose(a, b, atol=1e-12, rtol=0)
+
+
+def pin_bwd_finite_differences(mod):
+    # a packed batch with a two-sided window, unequal lengths and an empty sequence:
+    # gradients of L = sum(O * W) against central differences
+    lq, lk = [5, 0, 7], [9, 3, 4]
+    q, k, v, cq, ck = _packed(24, lq, lk, Hq=2, Hkv=1, d=3)
+    W = randn(28, q.shape, torch.float32).double().numpy()
+    window = (3, 1)
+    dq, dk, dv = mod.attention_bwd_masked(q, k, v, W, 0.6, cq, ck, window)
+
+    def loss(qq, kk, vv):
+        O, _ = mod.attention_fwd_masked(qq, kk, vv, 0.6, cq, ck, window)
+        return float((O * W).sum())
+
+    eps = 1e-6
+    for X, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = [Xp if Y is X else Y for Y in (q, k, v)]
+            args_m = [Xm if Y is X else Y for Y in (q, k, v)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, g[idx])
+
+
+def pin_bwd_unseen_keys_and_empty_rows(mod):
+    # window (0, 0) with Nq = Nk: each query sees only its own key; with Nk > Nq the first
+    # Nk - Nq keys are seen by nobody (zero dK, dV); with Nq > Nk the first rows see none
+    q, k, v = _fixed(30, Hq=2, Hkv=1, Nq=10, Nk=14, d=4)
+    do = randn(33, q.shape, torch.float32).double().numpy()
+    dq, dk, dv = mod.attention_bwd_masked(q, k, v, do, 0.5, window=(0, 0))
+    assert np.all(dk[:, :, :4] == 0) and np.all(dv[:, :, :4] == 0)
+    # a single visible key per row: softmax is 1, so dV_j = sum of dO over the rows that see j
+    assert np.allclose(dv[0, 0, 4:], do[0, 0] + do[0, 1], atol=1e-13)
+    assert np.allclose(dq, 0, atol=1e-13)        # P = 1 exactly: no dependence on the scores
+    q2, k2, v2 = _fixed(31, Hq=2, Hkv=1, Nq=12, Nk=5, d=4)
+    do2 = randn(34, q2.shape, torch.float32).double().numpy()
+    dq2, _, _ = mod.attention_bwd_masked(q2, k2, v2, do2, 0.5, window=(-1, 0))
+    assert np.all(dq2[:, :, :7] == 0)
+
+
 PINS = [pin_reduces_to_square_oracle, pin_short_queries_bottom_right, pin_long_queries, pin_packed_is_per_sequence,
-        pin_window_closed_form, pin_block_lists, pin_empty_sequences, pin_scalar_brute_force, pin_pair_counts]
+        pin_window_closed_form, pin_block_lists, pin_empty_sequences, pin_scalar_brute_force, pin_pair_counts,
+        pin_bwd_reduces_to_square_oracle, pin_bwd_finite_differences, pin_bwd_unseen_keys_and_empty_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -180,6 +232,9 @@ MUTANTS = {
     "packed_keys_from_query_offsets": ("K[h // G, ks:ke], V[h // G, ks:ke]", "K[h // G, qs:qe], V[h // G, qs:qe]"),
     "gqa_modulo": ("_attend(Q[b, h, r], K[b, h // G], V[b, h // G]", "_attend(Q[b, h, r], K[b, h % Hkv], V[b, h % Hkv]"),
     "block_list_first_head_always": ("kl = hm[0] if len(hm) == 1 else hm[h]", "kl = hm[0]"),
+    "bwd_without_jacobian_term": ("dS = P * (dP - Dr[:, None])", "dS = P * dP"),
+    "bwd_dk_unscaled": ("dKb = scale * (dS.T @ Qb)", "dKb = dS.T @ Qb"),
+    "bwd_ignores_window": ("vis = visible(Qb.shape[0], Kb.shape[0], window)", "vis = visible(Qb.shape[0], Kb.shape[0])"),
 }
 
 
