@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     FaError,
     block_lists_to_tensors,
     bwd,
+    bwd_masked,
     bwd_workspace_size,
     declared_symbols,
     fp8_prepare,

@@ -62,6 +62,11 @@ def load() -> ctypes.CDLL:
     L.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                 _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp]
     L.fa_fwd_masked.restype = ctypes.c_int
+    L.fa_bwd_masked_workspace_size.argtypes = [_i64, _i64, _i64]
+    L.fa_bwd_masked_workspace_size.restype = ctypes.c_size_t
+    L.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64,
+                                _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float, _vp]
+    L.fa_bwd_masked.restype = ctypes.c_int
     L.fa_fp8_v_codes_bytes.argtypes = [_i64, _i64, _i64, _i64]
     L.fa_fp8_v_codes_bytes.restype = ctypes.c_size_t
     L.fa_fp8_quantize_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, _i64, _vp]
@@ -429,3 +434,43 @@ def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_
     if st != FA_OK:
         _raise(st)
     return o, lse_t
+
+
+def bwd_masked(q, k, v, o, lse, do, window=(-1, -1), softmax_scale: float | None = None, cu_seqlens_q=None,
+               cu_seqlens_k=None, max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
+               workspace: torch.Tensor | None = None):
+    """dQ, dK, dV under the mask family via fa_bwd_masked (layouts as in fwd_masked)."""
+    L = load()
+    packed = cu_seqlens_q is not None
+    dev = q.device
+    if packed:
+        Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[0], k.shape[1]
+        B = cu_seqlens_q.numel() - 1
+        mq = Nq if max_seqlen_q is None else int(max_seqlen_q)
+        mk = Nk if max_seqlen_k is None else int(max_seqlen_k)
+        for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+            _check(t, n, dev, torch.int32)
+    else:
+        B, Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[1], k.shape[2]
+        mq, mk = Nq, Nk
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, dev, q.dtype)
+    _check(lse, "lse", dev, torch.float32)
+    if o.shape != q.shape or do.shape != q.shape or k.shape != v.shape:
+        raise ValueError("o and do must match q; k and v must match")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    need = L.fa_bwd_masked_workspace_size(B, Hq, mq)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Nq,
+                             Nk, d, _dtype_code(q), ptr(cu_seqlens_q), ptr(cu_seqlens_k), mq, mk, int(window[0]),
+                             int(window[1]), scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return dq, dk, dv

@@ -166,6 +166,44 @@ fa_status run_fp8_quant(const void* x, const float* signs, void* codes, float* s
   return FA_OK;
 }
 
+// Validation shared by the mask-family entry points; fills the common fields of args.
+template <class Args>
+fa_status check_masked(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype,
+                       const int32_t* cu_q, const int32_t* cu_k, int64_t max_q, int64_t max_k, int64_t wl,
+                       int64_t wr, float scale, bool* empty, Args& a) {
+  const bool packed = cu_q != nullptr || cu_k != nullptr;
+  if (packed && (cu_q == nullptr || cu_k == nullptr))
+    return fail(FA_ERR_INVALID_ARGUMENT, "give both cu_seqlens_q and cu_seqlens_k, or neither");
+  if (Nk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "Nk must be >= 0 (Nk=%lld)", (long long)Nk);
+  fa_status st = check_sizes(B, Hq, Hkv, std::max(Nq, Nk), d, dtype, empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  const int64_t maxq = packed ? max_q : Nq, maxk = packed ? max_k : Nk;
+  if (packed && (max_q < 0 || max_k < 0 || max_q > Nq || max_k > Nk))
+    return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen_q/k must be in [0, Nq] / [0, Nk] (got %lld, %lld)",
+                (long long)max_q, (long long)max_k);
+  if (wl < -1 || wr < -1 || wl > INT_MAX / 2 || wr > INT_MAX / 2)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be -1 (unbounded) or >= 0 (got %lld, %lld)",
+                (long long)wl, (long long)wr);
+  if (packed && ((st = check_ptr4(cu_q, "cu_seqlens_q")) != FA_OK || (st = check_ptr4(cu_k, "cu_seqlens_k")) != FA_OK))
+    return st;
+  *empty = *empty || B == 0 || maxq == 0;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.N = (int)Nq;
+  a.Nk = (int)Nk;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.maxq = (int)maxq;
+  a.maxk = (int)maxk;
+  a.wl = (int)wl;
+  a.wr = (int)wr;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,61 +388,76 @@ fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* block_idx, int64_t block_heads, float softmax_scale,
                         struct ihipStream_t* stream) {
   g_last_error[0] = '\0';
-  const bool packed = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
-  if (packed && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr))
-    return fail(FA_ERR_INVALID_ARGUMENT, "give both cu_seqlens_q and cu_seqlens_k, or neither");
-  if (Nk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "Nk must be >= 0 (Nk=%lld)", (long long)Nk);
   bool empty = false;
-  fa_status st = check_sizes(B, Hq, Hkv, std::max(Nq, Nk), d, dtype, &empty);
+  fa::FwdArgs a;
+  fa_status st = check_masked(B, Hq, Hkv, Nq, Nk, d, dtype, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              window_left, window_right, softmax_scale, &empty, a);
   if (st != FA_OK) return st;
-  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
-  const int64_t maxq = packed ? max_seqlen_q : Nq, maxk = packed ? max_seqlen_k : Nk;
-  if (packed && (max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > Nq || max_seqlen_k > Nk))
-    return fail(FA_ERR_INVALID_ARGUMENT, "max_seqlen_q/k must be in [0, Nq] / [0, Nk] (got %lld, %lld)",
-                (long long)max_seqlen_q, (long long)max_seqlen_k);
-  if (window_left < -1 || window_right < -1 || window_left > INT_MAX / 2 || window_right > INT_MAX / 2)
-    return fail(FA_ERR_INVALID_ARGUMENT, "window sides must be -1 (unbounded) or >= 0 (got %lld, %lld)",
-                (long long)window_left, (long long)window_right);
   if ((block_cnt == nullptr) != (block_idx == nullptr))
     return fail(FA_ERR_INVALID_ARGUMENT, "give both block_cnt and block_idx, or neither");
   if (block_idx != nullptr && block_heads != 1 && block_heads != Hq)
     return fail(FA_ERR_INVALID_ARGUMENT, "block_heads must be 1 or Hq (got %lld)", (long long)block_heads);
-  if (B == 0 || maxq == 0 || Hq == 0) return FA_OK;
+  if (empty) return FA_OK;
   if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK)
     return st;
   if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK)) return st;
-  if (packed && ((st = check_ptr4(cu_seqlens_q, "cu_seqlens_q")) != FA_OK ||
-                 (st = check_ptr4(cu_seqlens_k, "cu_seqlens_k")) != FA_OK))
-    return st;
   if (block_idx != nullptr && ((st = check_ptr4(block_cnt, "block_cnt")) != FA_OK ||
                                (st = check_ptr4(block_idx, "block_idx")) != FA_OK))
     return st;
-  fa::FwdArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.lse = lse;
-  a.B = (int)B;
-  a.Hq = (int)Hq;
-  a.Hkv = (int)Hkv;
-  a.N = (int)Nq;
-  a.Nk = (int)Nk;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * kLog2e;
-  a.cu_q = cu_seqlens_q;
-  a.cu_k = cu_seqlens_k;
-  a.maxq = (int)maxq;
-  a.maxk = (int)maxk;
-  a.wl = (int)window_left;
-  a.wr = (int)window_right;
   a.bcnt = block_cnt;
   a.bidx = block_idx;
   a.bheads = block_idx ? (int)block_heads : 1;
-  a.bnq = (int)((maxq + 255) / 256);
-  a.bcap = (int)((maxk + 63) / 64);
+  a.bnq = (a.maxq + 255) / 256;
+  a.bcap = (a.maxk + 63) / 64;
   const hipError_t err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "masked forward launch failed: %s", hipGetErrorString(err));
+  return FA_OK;
+}
+
+size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t max_seqlen_q) {
+  if (B < 0 || Hq < 0 || max_seqlen_q < 0) return 0;
+  return fa::bwd_rowterm_bytes(B, Hq, max_seqlen_q);
+}
+
+fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t max_seqlen_q,
+                        int64_t max_seqlen_k, int64_t window_left, int64_t window_right, float softmax_scale,
+                        struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa::BwdArgs a;
+  fa_status st = check_masked(B, Hq, Hkv, Nq, Nk, d, dtype, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              window_left, window_right, softmax_scale, &empty, a);
+  if (st != FA_OK || empty) return st;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK ||
+      (st = check_ptr(dout, "dout")) != FA_OK || (st = check_ptr(dq, "dq")) != FA_OK ||
+      (st = check_ptr(workspace, "workspace")) != FA_OK)
+    return st;
+  if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK ||
+                 (st = check_ptr(dk, "dk")) != FA_OK || (st = check_ptr(dv, "dv")) != FA_OK))
+    return st;
+  const size_t need = fa::bwd_rowterm_bytes(B, Hq, a.maxq);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.rowterm = static_cast<float*>(workspace);
+  const hipError_t err = fa::launch_bwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "masked backward launch failed: %s", hipGetErrorString(err));
   return FA_OK;
 }
 

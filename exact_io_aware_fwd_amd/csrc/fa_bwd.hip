@@ -44,19 +44,31 @@ __host__ __device__ inline long long rowterm_index(long long bh, int nb32, int r
 }
 
 // ---- 1. row terms: LSE_i * log2 e and -D_i = -sum_k dO_ik O_ik per query row ----------
-template <class Tag, int D>
+// GEN (the mask family): rows are padded per (batch, head) to ceil(maxq/32) blocks; a
+// packed batch takes sequence b's rows from cu_q[b]; a row that saw no key (LSE = -inf)
+// stores 0, and all its scores are masked in the passes below.
+template <class Tag, int D, bool GEN = false>
 __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long long prows) {
   using E = Elt<Tag>;
   constexpr int TPR = D / 8;   // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const int N = a.N;
-  const int nb32 = (N + 31) / 32;
+  const int nb32 = ((GEN ? a.maxq : N) + 31) / 32;
   const long long p = (long long)blockIdx.x * RPB + threadIdx.x / TPR;   // padded row
   const long long bh = p / (32LL * nb32);
   const int r = (int)(p - bh * 32LL * nb32);
   const int part = threadIdx.x % TPR;
-  const bool real = p < prows && r < N;
-  const long long row = bh * N + r;
+  int Lr = N;
+  long long row = bh * N + r;
+  if constexpr (GEN) {
+    if (a.cu_q != nullptr && p < prows) {
+      const int b = (int)(bh / a.Hq), h = (int)(bh - (long long)b * a.Hq);
+      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
+      Lr = min(qe - qs, a.maxq);
+      row = (long long)h * N + qs + r;
+    }
+  }
+  const bool real = p < prows && r < Lr;
   float acc = 0.f;
   if (real) {
     const u32x4 o4 = *(const u32x4*)((const unsigned char*)a.o + (row * D + part * 8) * 2);
@@ -71,7 +83,8 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, TPR);
   if (p < prows && part == 0) {
     const long long t = rowterm_index(bh, nb32, r);
-    a.rowterm[t] = real ? a.lse[row] * kLog2e : 0.f;
+    const float l = real ? a.lse[row] : 0.f;
+    a.rowterm[t] = (real && (!GEN || l > -INFINITY)) ? l * kLog2e : 0.f;
     a.rowterm[t + 32] = real ? -acc : 0.f;
   }
 }
@@ -101,7 +114,7 @@ __device__ __forceinline__ void dkdv_dma(const unsigned char* qh, const unsigned
   }
 }
 
-template <class Tag, int D, bool CAUSAL>
+template <class Tag, int D, bool CAUSAL, bool GEN = false>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
@@ -149,14 +162,36 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     grp = blockIdx.x - jb * ngroups;
   }
   const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  // sequence geometry: Lq queries, Lk keys; qrow0 = first Q row of query head hkv*G,
+  // hs = rows between query heads
+  int Lq = N, Lk = N;
+  size_t kvhead, qrow0, hs = (size_t)N;
+  if constexpr (GEN) {
+    if (a.cu_q != nullptr) {
+      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
+      const int ks = min(max(a.cu_k[b], 0), a.Nk), ke = min(max(a.cu_k[b + 1], ks), a.Nk);
+      Lq = min(qe - qs, a.maxq);
+      Lk = min(ke - ks, a.maxk);
+      kvhead = (size_t)hkv * (size_t)a.Nk + ks;
+      qrow0 = (size_t)hkv * G * (size_t)N + qs;
+    } else {
+      Lk = a.Nk;
+      kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+      qrow0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
+    }
+  } else {
+    kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+    qrow0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
+  }
   const int k0 = jb * BKV;
+  if (GEN && k0 >= Lk) return;        // the whole workgroup: past this sequence's keys
   const int kw = k0 + 32 * wave;      // first key of this wave
   const int mykey = kw + r32;         // the key this lane's scores belong to
+  const int off = Lk - Lq;            // query i sits at key position i + off
 
   // K^T and V^T as B operands: lane holds row mykey, elements 16s + 8hh .. +7
   u32x4 kf[NS], vf[NS];
-  if (mykey < N) {
+  if (mykey < Lk) {
     const unsigned char* kp = (const unsigned char*)a.k + (kvhead + mykey) * ROWB + 16 * hh;
     const unsigned char* vp = (const unsigned char*)a.v + (kvhead + mykey) * ROWB + 16 * hh;
 #pragma unroll
@@ -170,12 +205,22 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   // Steps: for each query head of the group, query blocks from the last down to the
-  // first one that meets these keys (the key block's own start when causal).
-  const int nb32 = (N + 31) / 32;
-  const int qtop = (nb32 - 1) * BQ;
-  const int qlo = CAUSAL ? k0 : 0;
-  const int per_head = (qtop - qlo) / BQ + 1;
-  const int nsteps = G * per_head;
+  // first one that meets these keys (the key block's own start when causal; under a
+  // window, the blocks of queries whose window meets the block's keys).
+  const int nb32 = ((GEN ? a.maxq : N) + 31) / 32;
+  int qtop, qlo, nsteps;
+  if constexpr (GEN) {
+    const int kmax = min(k0 + BKV, Lk) - 1;
+    const int iq_lo = a.wr >= 0 ? max(k0 - a.wr - off, 0) : 0;
+    const int iq_hi = a.wl >= 0 ? min(kmax + a.wl - off, Lq - 1) : Lq - 1;
+    qtop = iq_hi >= 0 ? iq_hi / BQ * BQ : 0;
+    qlo = iq_lo / BQ * BQ;
+    nsteps = iq_lo <= iq_hi ? G * ((qtop - qlo) / BQ + 1) : 0;
+  } else {
+    qtop = (nb32 - 1) * BQ;
+    qlo = CAUSAL ? k0 : 0;
+    nsteps = G * ((qtop - qlo) / BQ + 1);
+  }
 
   // ---- HBM -> LDS (step n into slot n % 3), driven by a cursor over (head, block) ----
   int soff[LI];
@@ -185,19 +230,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     const int row = (nn % TI) * RPI + lane / CH;
     soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
   }
-  const size_t qhead0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
-  const unsigned char* dq_h = (const unsigned char*)a.q + qhead0 * ROWB;
-  const unsigned char* dg_h = (const unsigned char*)a.dout + qhead0 * ROWB;
+  const unsigned char* dq_h = (const unsigned char*)a.q + qrow0 * ROWB;
+  const unsigned char* dg_h = (const unsigned char*)a.dout + qrow0 * ROWB;
   const float* dr_h = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
-  const int hbytes = N * ROWB, rbytes = nb32 * 256;
+  const int hbytes = Lq * ROWB, rbytes = nb32 * 256;   // buffer ranges: rows past Lq read 0
   int dqb = qtop;   // query block of the next step to load
   auto dma_next = [&](unsigned char* sl) __attribute__((always_inline)) {
     dkdv_dma<ROWB, TI, LI, NW, TB>(dq_h, dg_h, dr_h, hbytes, rbytes, dqb * ROWB, dqb * 8, wave, lane, soff, sl);
     dqb -= BQ;
     if (dqb < qlo) {
       dqb = qtop;
-      dq_h += hbytes;
-      dg_h += hbytes;
+      dq_h += hs * ROWB;
+      dg_h += hs * ROWB;
       dr_h += nb32 * 64;
     }
   };
@@ -286,16 +330,36 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     l2n = rt16(bn, 0);
-    const bool active = !CAUSAL || cqb >= kw;
+    bool active, full;
+    if constexpr (GEN) {
+      // wave-uniform: does any (query, key) pair of this step and wave meet, do all?
+      const int qmax = min(cqb + BQ, Lq) - 1, kmax = min(kw + 32, Lk) - 1;
+      const int vlo = a.wl >= 0 ? cqb + off - a.wl : 0;              // keys some query sees
+      const int vhi = a.wr >= 0 ? qmax + off + a.wr : Lk - 1;
+      active = kw <= kmax && cqb <= qmax && max(vlo, kw) <= min(vhi, kmax);
+      full = kw + 31 < Lk && cqb + BQ - 1 < Lq && (a.wl < 0 || qmax + off - a.wl <= kw) &&
+             (a.wr < 0 || kw + 31 <= cqb + off + a.wr);
+    } else {
+      active = !CAUSAL || cqb >= kw;
+      full = !CAUSAL || cqb != kw;
+    }
     if (active) {
-      if (CAUSAL && cqb == kw) {
-        // diagonal block: query 8(v/4) + 4hh + v%4 sees key r32 only if r32 <= query
+      if (!full) {
+        // query cqb + 8(v/4) + 4hh + v%4 against this lane's key: outside the mask -> 0
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (r32 > 8 * (v >> 2) + 4 * hh + (v & 3)) {
+        for (int v = 0; v < 16; ++v) {
+          const int qi = cqb + 8 * (v >> 2) + 4 * hh + (v & 3);
+          bool vis;
+          if constexpr (GEN)
+            vis = qi < Lq && mykey < Lk && (a.wl < 0 || mykey >= qi + off - a.wl) &&
+                  (a.wr < 0 || mykey <= qi + off + a.wr);
+          else
+            vis = mykey <= qi;
+          if (!vis) {
             sc[v] = 0.f;
             dpc[v] = 0.f;
           }
+        }
       }
       const u32x4 pf[2] = {pack(sc, 0), pack(sc, 1)};
       const u32x4 sf[2] = {pack(dpc, 0), pack(dpc, 1)};
@@ -367,7 +431,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   acc_drain(dv);
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T, rounded to the input dtype
-  if (mykey < N) {
+  if (mykey < Lk) {
     unsigned char* dKg = (unsigned char*)a.dk + (kvhead + mykey) * ROWB;
     unsigned char* dVg = (unsigned char*)a.dv + (kvhead + mykey) * ROWB;
 #pragma unroll
@@ -386,7 +450,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---- 2. dQ per query block -------------------------------------------------------------
-template <class Tag, int D, bool CAUSAL, int NW>
+template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
 __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
@@ -418,21 +482,40 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   const int N = a.N;
 
   int b, hq, iq;
-  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  map_q_block(((GEN ? a.maxq : N) + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
   const int hkv = hq / (a.Hq / a.Hkv);
-  const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  int Lq = N, Lk = N;
+  size_t qhead, kvhead;
+  if constexpr (GEN) {
+    if (a.cu_q != nullptr) {
+      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
+      const int ks = min(max(a.cu_k[b], 0), a.Nk), ke = min(max(a.cu_k[b + 1], ks), a.Nk);
+      Lq = min(qe - qs, a.maxq);
+      Lk = min(ke - ks, a.maxk);
+      qhead = (size_t)hq * (size_t)N + qs;
+      kvhead = (size_t)hkv * (size_t)a.Nk + ks;
+    } else {
+      Lk = a.Nk;
+      qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+      kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+    }
+  } else {
+    qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+    kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  }
   const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
   const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
 
   const int q0 = iq * BR;
+  if (GEN && q0 >= Lq) return;         // the whole workgroup: past this sequence's queries
   const int qw = q0 + wave * 32;
   const int myq = qw + r32;            // the query this lane's scores belong to
+  const int off = Lk - Lq;
 
   // Q^T and dO^T as B operands: lane holds row myq, elements 16s + 8hh .. +7
   u32x4 qf[NS], df[NS];
   float lse2 = 0.f, negd = 0.f;
-  if (myq < N) {
+  if (myq < Lq) {
     const unsigned char* qp = (const unsigned char*)a.q + (qhead + myq) * ROWB + 16 * hh;
     const unsigned char* gp = (const unsigned char*)a.dout + (qhead + myq) * ROWB + 16 * hh;
 #pragma unroll
@@ -440,7 +523,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       qf[s] = *(const u32x4*)(qp + 32 * s);
       df[s] = *(const u32x4*)(gp + 32 * s);
     }
-    const long long t = rowterm_index((long long)b * a.Hq + hq, (N + 31) / 32, myq);
+    const long long t = rowterm_index((long long)b * a.Hq + hq, ((GEN ? a.maxq : N) + 31) / 32, myq);
     lse2 = a.rowterm[t];
     negd = a.rowterm[t + 32];
   } else {
@@ -452,13 +535,36 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) ndv[i] = negd;
 
-  const int nkv = (N + BC - 1) / BC;
-  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+  const int nkv = (Lk + BC - 1) / BC;
+  // key tiles t_lo + j, j < ntile; under a window, masked head [0, JH), plain [JH, JT),
+  // masked tail [JT, ntile) (a tile's flag covers its own two units)
+  int ntile, t_lo = 0, JH = 0, JT = 0;
+  int lo_q = 0, hi_q = Lk - 1, wlo = 0, whi;
+  if constexpr (GEN) {
+    const int qlast = min(q0 + BR, Lq) - 1;
+    auto lo_of = [&](int i) { return a.wl >= 0 ? i + off - a.wl : 0; };
+    auto hi_of = [&](int i) { return a.wr >= 0 ? min(i + off + a.wr, Lk - 1) : Lk - 1; };
+    lo_q = lo_of(myq);
+    hi_q = hi_of(myq);
+    wlo = max(lo_of(min(qw + 31, Lq - 1)), 0);
+    whi = hi_of(qw);
+    const int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
+    t_lo = klo / BC;
+    const int t_hi = (Lk <= 0 || khi < klo) ? t_lo : khi / BC + 1;
+    ntile = t_hi - t_lo;
+    const int P1 = min(max((max(lo_of(qlast), 0) + BC - 1) / BC - t_lo, 0), ntile);
+    const int P2 = min(max((hi_of(q0) + 1) / BC - t_lo, 0), ntile);
+    JH = min(ntile, (P1 + 2) / 3 * 3);
+    JT = max(JH, P2 / 3 * 3);
+  } else {
+    ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+    whi = CAUSAL ? min(qw, N - 1) : N - 1;
+  }
 
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
   auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
-    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+    Tiles::load(Kg, Vg, Lk, GEN ? t_lo + t : t, wave, doff, sl);
   };
 
   // per-lane LDS offsets: K rows (swizzled) and V rows (A operands of S^T, dP^T), K
@@ -535,13 +641,19 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       dpn = E::mma(vc, df[k], k == 0 ? ndv : dpn);
       if (k == NS - 1) {
         if constexpr (decltype(MASK)::value) {
-          // keys 32u + 8(v/4) + 4hh + v%4 of this lane's column
-          const int k0 = u * 32;
-          int lim = N - k0 - 4 * hh;
-          if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+          // keys k0 + 8(v/4) + 4hh + v%4 of this lane's column; a unit every query of the
+          // wave sees whole needs nothing
+          const int k0 = (GEN ? t_lo * 2 + u : u) * 32;
+          if (!(k0 >= wlo && k0 + 31 <= whi)) {
+            int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;
+            if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+            const int llo = lo_q - k0 - 4 * hh;
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = 0.f;
+            for (int v = 0; v < 16; ++v) {
+              const int o = 8 * (v >> 2) + (v & 3);
+              if (o >= lim || (GEN && o < llo)) sc[v] = 0.f;
+            }
+          }
         }
         pf[0] = pack(sc, 0);
         pf[1] = pack(sc, 1);
@@ -575,6 +687,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   using Plain = std::false_type;
   using Masked = std::true_type;
 
+  if (!GEN || ntile > 0) {   // (a mask-family workgroup may have no key tile)
   dma(0, slot0);
   if (ntile > 1) dma(1, slot1);
   wait_loads();
@@ -587,10 +700,20 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     pa = E::mma(vrow(slot0, 0, st), df[st], pa);
   }
   // Tiles whose units all precede every wave's last unit need no mask.
-  const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
-  const int J1 = min(ntile, ulast0 / 2) / 3 * 3;
+  if constexpr (!GEN) {
+    const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
+    JT = min(ntile, ulast0 / 2) / 3 * 3;
+  }
   int j = 0;
-  for (; j < J1; j += 3) {
+  for (; j < JH; j += 3) {
+    tile(I0{}, Masked{}, j);
+    if (j + 1 >= ntile) break;
+    tile(I1{}, Masked{}, j + 1);
+    if (j + 2 >= ntile) break;
+    tile(I2{}, Masked{}, j + 2);
+  }
+  j = JH;
+  for (; j < JT; j += 3) {
     tile(I0{}, Plain{}, j);
     tile(I1{}, Plain{}, j + 1);
     tile(I2{}, Plain{}, j + 2);
@@ -602,10 +725,11 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     if (j + 2 >= ntile) break;
     tile(I2{}, Masked{}, j + 2);
   }
+  }
   acc_drain(acc);
 
   // dQ = scale * (dQ^T)^T, rounded to the input dtype
-  if (myq < N) {
+  if (myq < Lq) {
     unsigned char* Og = (unsigned char*)a.dq + (qhead + myq) * ROWB;
     const float sc = a.scale;
 #pragma unroll
@@ -641,6 +765,33 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+template <class Tag, int D>
+static hipError_t launch_bwd_masked_t(const BwdArgs& a, hipStream_t stream) {
+  const long long prows = (long long)a.B * a.Hq * ((a.maxq + 31) / 32) * 32;   // padded rows
+  if (prows <= 0) return hipSuccess;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_rowterm_kernel<Tag, D, true>), dim3((unsigned)((prows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, a, prows);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  constexpr int NWQ = D == 128 ? 4 : 8;
+  const long long nqb = (a.maxq + 32 * NWQ - 1) / (32 * NWQ);
+  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, false, NWQ, true>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(NWQ * 64),
+                     0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const long long nkb = (a.maxk + 127) / 128;
+  if (nkb <= 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, false, true>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_masked(const BwdArgs& a, int d, bool bf16, hipStream_t stream) {
+  if (bf16) return d == 128 ? launch_bwd_masked_t<bf16_tag, 128>(a, stream) : launch_bwd_masked_t<bf16_tag, 64>(a, stream);
+  return d == 128 ? launch_bwd_masked_t<f16_tag, 128>(a, stream) : launch_bwd_masked_t<f16_tag, 64>(a, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream) {

@@ -42,6 +42,13 @@ struct BwdArgs {
   int B, Hq, Hkv, N;
   float scale;
   float scale_log2;
+  // Mask family (the general kernels only), as in FwdArgs; the row terms are padded per
+  // (batch, head) to ceil(maxq / 32) blocks.
+  int Nk = 0;
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int maxq = 0, maxk = 0;
+  int wl = -1, wr = -1;
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
@@ -121,6 +128,7 @@ struct Fp8FwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_fwd_masked(const FwdArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_bwd_masked(const BwdArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_splitkv(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 // mode 0: rows with the transform, 1: rows, 2: value tiles
 hipError_t launch_fp8_quant(const QuantArgs& a, int d, bool bf16, int mode, hipStream_t stream);

@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
                           "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_num_splits",
                           "fa_lse_combine", "fa_fp8_v_codes_bytes", "fa_fp8_quantize_rows", "fa_fp8_quantize_v",
-                          "fa_fwd_fp8", "fa_fwd_masked"}
+                          "fa_fwd_fp8", "fa_fwd_masked", "fa_bwd_masked",
+                          "fa_bwd_masked_workspace_size"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -237,3 +238,26 @@ def test_fwd_masked_rejects(L, kw, expect):
 def test_fwd_masked_empty(L):
     assert masked(L, B=0) == OK and masked(L, Nq=0) == OK
     assert masked(L, cq=P, ck=P, mq=0, mk=5) == OK        # every sequence empty
+
+
+def bwd_masked(L, ws_bytes=1 << 20, B=1, Hq=2, Hkv=1, Nq=100, Nk=120, d=128, dtype=1, cq=None, ck=None, mq=0, mk=0,
+               wl=-1, wr=-1, scale=0.125, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws")}
+    p.update(ptrs)
+    return L.fa_bwd_masked(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"], p["ws"],
+                           ws_bytes, B, Hq, Hkv, Nq, Nk, d, dtype, cq, ck, mq, mk, wl, wr, scale, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dq=None), INV), (dict(ws=None), INV), (dict(ws_bytes=64), INV), (dict(cq=P), INV), (dict(wl=-3), INV),
+    (dict(cq=P, ck=P, mq=500, mk=10), INV), (dict(d=96), UNS), (dict(Hq=3, Hkv=2), INV), (dict(scale=0.0), INV),
+])
+def test_bwd_masked_rejects(L, kw, expect):
+    assert bwd_masked(L, **kw) == expect
+    assert binding.last_error() != ""
+
+
+def test_bwd_masked_workspace_and_empty(L):
+    # row terms per (sequence, head), padded to 32-row blocks: 256 bytes per block
+    assert L.fa_bwd_masked_workspace_size(3, 4, 100) == 3 * 4 * 4 * 256
+    assert bwd_masked(L, B=0) == OK and bwd_masked(L, Nq=0) == OK
