@@ -45,7 +45,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward pass (profiling)")
@@ -81,6 +81,20 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
+
+
+def warm_up(step, min_steps: int, min_seconds: float = 0.3) -> int:
+    """Run `step` at least min_steps times and for at least min_seconds of GPU time (the
+    clocks of an idle GPU take a while to ramp); returns the number of calls made."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < min_steps or time.perf_counter() - t0 < min_seconds:
+        step()
+        n += 1
+        if n % 8 == 0 or n >= min_steps:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def source_hash(kind: str) -> str:
@@ -221,9 +235,7 @@ def bench_decode(args):
     def step():
         fa.binding.fwd_splitkv(q, k, v, causal=causal, softmax_scale=w.scale, workspace=ws, out=o, lse=lse)
 
-    for _ in range(max(args.warmup, 5)):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, max(args.warmup, 5))
     steps = max(args.steps, 50)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -239,7 +251,7 @@ def bench_decode(args):
     gbps = nbytes / (ms * 1e-3) / 1e9
     rec = {
         "metric": "split-KV decoding attention: HBM GB/s and % of peak",
-        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": nwarm,
         "ms_per_step": wall * 1e3 / steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16"}[q.dtype], "data": "synthetic (seeded iid N(0,1))",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
@@ -302,10 +314,7 @@ def bench_fp8(args):
         fa.fwd_fp8(*ops[0], causal=causal, softmax_scale=w.scale, block_q=w.block_q, block_kv=w.block_kv,
                    out=o, lse=lse)
 
-    for _ in range(max(args.warmup, 3)):
-        quantise()
-        attend()
-    torch.cuda.synchronize()
+    nwarm = warm_up(lambda: (quantise(), attend()), max(args.warmup, 3))
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -326,7 +335,7 @@ def bench_fp8(args):
     qbytes = metrics.fp8_quant_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, 2, w.block_q, w.block_kv)
     rec = {
         "metric": "FP8 attention forward TFLOPS and % of the FP8 matrix-core peak at N=8192 d=128 causal",
-        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, 3),
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": nwarm,
         "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8 e4m3 operands, fp32 accumulation, bf16 output",
         "data": "synthetic (seeded N(0,1), 0.1% of entries x16; random signs)",
@@ -393,10 +402,10 @@ def bench_masks(args):
         flops = 4.0 * w.d * w.Hq * pairs
         return run, flops, (q, k, v, cq, ck, lists)
 
+    nwarms = []
+
     def timed(run, steps):
-        for _ in range(max(args.warmup, 3)):
-            run()
-        torch.cuda.synchronize()
+        nwarms.append(warm_up(run, max(args.warmup, 3)))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
@@ -411,6 +420,16 @@ def bench_masks(args):
     ms, wall_ms = timed(run, args.steps)
     achieved = flops / (ms * 1e-3) / 1e12
     passes = {}
+    if not w.packed and not w.block and not args.headline_only:
+        # the backward of the same masked problem (five products per visible pair)
+        qd, kd, vd = (t.to(dev) for t in cpu_inputs[:3])
+        do = workloads.randn(w.seeds[0] + 50, tuple(qd.shape), qd.dtype).to(dev)
+        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale)
+        ws = torch.empty(fa.binding.load().fa_bwd_masked_workspace_size(w.B, w.Hq, w.seqlens_q[0]),
+                         dtype=torch.uint8, device=dev)
+        mb, _ = timed(lambda: fa.bwd_masked(qd, kd, vd, o, lse, do, w.window, w.scale, workspace=ws), args.steps)
+        passes[w.name + " backward"] = {"ms": mb, "TFLOPs": 2.5 * flops / (mb * 1e-3) / 1e12,
+                                        "visible_pair_flops": 2.5 * flops}
     for name in workloads.MASK_WORKLOADS:
         if name == w.name or name.startswith("mix_") or args.headline_only:
             continue
@@ -419,7 +438,7 @@ def bench_masks(args):
         passes[name] = {"ms": m2, "TFLOPs": f2 / (m2 * 1e-3) / 1e12, "visible_pair_flops": f2}
     rec = {
         "metric": "mask-family attention forward TFLOPS (visible pairs) and % of the MFMA peak, sliding window at N=8192 d=128",
-        "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, 3),
+        "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": nwarms[0],
         "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded iid N(0,1))",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.seqlens_q[0], "Nk": w.seqlens_k[0],
