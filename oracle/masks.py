@@ -34,8 +34,8 @@ Readings taken where the pages are silent (listed with the others in the design 
   the key tiles to visit; a score outside the listed tiles is masked.
 * A query that sees no key gets O = 0 and LSE = -inf.
 * Gradients ("FlashAttention Primer", section "Backward pass: recomputation instead of
-  storage", with the full softmax Jacobian as in :mod:`oracle.attention`): for every
-  visible pair, P = exp(S - LSE), dV += P^T dO, dP = dO V^T, D_i = sum_k dO_ik O_ik,
+  storage", with the full softmax Jacobian as in :mod:`oracle.attention`; the same mask,
+  block lists included, as the forward): for every visible pair, P = exp(S - LSE), dV += P^T dO, dP = dO V^T, D_i = sum_k dO_ik O_ik,
   dS = P * (dP - D), dQ = scale dS K, dK += scale dS^T Q; masked pairs and rows without
   keys contribute nothing; dK and dV of a K/V head sum over its query heads.
 
@@ -71,6 +71,14 @@ def visible(Lq: int, Lk: int, window=(-1, -1), kept_tiles=None, rows=None) -> np
                     tile_ok[qb, t] = True
         vis &= tile_ok[i // QBLOCK, (np.arange(Lk) // KTILE)[None, :]]
     return vis
+
+
+def _head_lists(block_lists, b: int, h: int):
+    """Key-tile lists (one per query block) of query head h of sequence b, or None."""
+    if block_lists is None:
+        return None
+    hm = block_lists[b]
+    return hm[0] if len(hm) == 1 else hm[h]
 
 
 def _attend(Q, K, V, vis, scale):
@@ -126,10 +134,7 @@ def attention_fwd_masked(q, k, v, scale: float, cu_seqlens_q=None, cu_seqlens_k=
     L = np.full(O.shape[:-1], -np.inf)
     for b in range(B):
         for h in range(Hq):
-            kl = None
-            if block_lists is not None:
-                hm = block_lists[b]
-                kl = hm[0] if len(hm) == 1 else hm[h]
+            kl = _head_lists(block_lists, b, h)
             if packed:
                 qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
                 vis = visible(qe - qs, ke - ks, window, kl)
@@ -150,12 +155,14 @@ def visible_pairs(Lqs, Lks, window=(-1, -1), block_lists_one_head=None) -> int:
     return n
 
 
-def attention_bwd_masked(q, k, v, do, scale: float, cu_seqlens_q=None, cu_seqlens_k=None, window=(-1, -1)):
-    """(dQ, dK, dV) in float64 of L(O) for O = attention_fwd_masked(q, k, v, ...) (no block
-    lists), with dO = dL/dO.  Layouts as in attention_fwd_masked."""
+def attention_bwd_masked(q, k, v, do, scale: float, cu_seqlens_q=None, cu_seqlens_k=None, window=(-1, -1),
+                         block_lists=None):
+    """(dQ, dK, dV) in float64 of L(O) for O = attention_fwd_masked(q, k, v, ...) with the
+    same lengths, window and block lists, and dO = dL/dO.  Layouts as in
+    attention_fwd_masked."""
     Q, K, V, dO = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     scale = float(scale)
-    O, LSE = attention_fwd_masked(Q, K, V, scale, cu_seqlens_q, cu_seqlens_k, window)
+    O, LSE = attention_fwd_masked(Q, K, V, scale, cu_seqlens_q, cu_seqlens_k, window, block_lists)
     packed = cu_seqlens_q is not None
     if packed:
         cq = np.asarray(cu_seqlens_q, dtype=np.int64)
@@ -168,12 +175,13 @@ def attention_bwd_masked(q, k, v, do, scale: float, cu_seqlens_q=None, cu_seqlen
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
     for b in range(B):
         for h in range(Hq):
+            kl = _head_lists(block_lists, b, h)
             if packed:
                 sq, sk = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
                 Qb, Kb, Vb, dOb, Ob, Lb = Q[h, sq], K[h // G, sk], V[h // G, sk], dO[h, sq], O[h, sq], LSE[h, sq]
             else:
                 Qb, Kb, Vb, dOb, Ob, Lb = Q[b, h], K[b, h // G], V[b, h // G], dO[b, h], O[b, h], LSE[b, h]
-            vis = visible(Qb.shape[0], Kb.shape[0], window)
+            vis = visible(Qb.shape[0], Kb.shape[0], window, kl)
             ok = np.isfinite(Lb)
             S = scale * (Qb @ Kb.T)
             P = np.where(vis & ok[:, None], np.exp(S - np.where(ok, Lb, 0.0)[:, None]), 0.0)

@@ -13,6 +13,11 @@
 * A scalar brute force (math.exp, math.fsum) over a packed batch with a window and
   block lists.
 * Pair counts: N(N+1)/2 for the square causal case, and the window's closed form.
+* Backward: reduces to the square backward oracle; central finite differences through
+  the forward (a packed batch with a window, and again with block lists that skip a
+  tile); closed forms for keys no query sees and rows with no key; with block lists,
+  each (head, query block) equals the backward of its queries against only its listed
+  keys, the key gradients summed over the blocks.
 Each planted mistake in MUTANTS must fail at least one pin.
 """
 from __future__ import annotations
@@ -213,9 +218,62 @@ def pin_bwd_unseen_keys_and_empty_rows(mod):
     assert np.all(dq2[:, :, :7] == 0)
 
 
+def pin_bwd_block_lists_as_deleted_keys(mod):
+    # full attention, per-head lists over two query blocks: each (head, query block) is the
+    # backward of its queries against only its listed keys; dK, dV of a key sum over the
+    # blocks that list it; unlisted keys and the rows of an empty list get zeros
+    Hq, Nq, Nk = 2, 300, 200
+    q, k, v = _fixed(40, Hq=Hq, Hkv=1, Nq=Nq, Nk=Nk, d=4)
+    do = randn(43, q.shape, torch.float32).double().numpy()
+    lists = [[[[0, 2], [1, 3]], [[3], []]]]
+    dq, dk, dv = mod.attention_bwd_masked(q, k, v, do, 0.4, block_lists=lists)
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(Hq):
+        for qb, tiles in enumerate(lists[0][h]):
+            if not tiles:
+                continue
+            rows = np.arange(256 * qb, min(256 * qb + 256, Nq))
+            keys = np.concatenate([np.arange(64 * t, min(64 * t + 64, Nk)) for t in tiles])
+            g = mod.attention_bwd_masked(q[:, h:h + 1, rows], k[:, :, keys], v[:, :, keys], do[:, h:h + 1, rows], 0.4)
+            eq[:, h:h + 1, rows] = g[0]
+            ek[:, :, keys] += g[1]
+            ev[:, :, keys] += g[2]
+    for a, b in zip((dq, dk, dv), (eq, ek, ev)):
+        assert np.allclose(a, b, atol=1e-12, rtol=0)
+    assert np.all(dq[0, 1, 256:] == 0)
+
+
+def pin_bwd_block_lists_finite_differences(mod):
+    # a packed batch with a window, unequal lengths and lists that skip a key tile the
+    # window would show: gradients of L = sum(O * W) against central differences
+    lq, lk = [6, 3], [150, 70]
+    q, k, v, cq, ck = _packed(44, lq, lk, Hq=1, Hkv=1, d=2)
+    W = randn(48, q.shape, torch.float32).double().numpy()
+    window = (100, 10)
+    lists = [[[[0, 2]]], [[[1]]]]
+    dq, dk, dv = mod.attention_bwd_masked(q, k, v, W, 0.7, cq, ck, window, lists)
+    assert np.all(dk[:, 64:128] == 0) and np.all(dv[:, 150:150 + 64] == 0)
+
+    def loss(qq, kk, vv):
+        O, _ = mod.attention_fwd_masked(qq, kk, vv, 0.7, cq, ck, window, lists)
+        return float((O * W).sum())
+
+    eps = 1e-6
+    for X, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = [Xp if Y is X else Y for Y in (q, k, v)]
+            args_m = [Xm if Y is X else Y for Y in (q, k, v)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, g[idx])
+
+
 PINS = [pin_reduces_to_square_oracle, pin_short_queries_bottom_right, pin_long_queries, pin_packed_is_per_sequence,
         pin_window_closed_form, pin_block_lists, pin_empty_sequences, pin_scalar_brute_force, pin_pair_counts,
-        pin_bwd_reduces_to_square_oracle, pin_bwd_finite_differences, pin_bwd_unseen_keys_and_empty_rows]
+        pin_bwd_reduces_to_square_oracle, pin_bwd_finite_differences, pin_bwd_unseen_keys_and_empty_rows,
+        pin_bwd_block_lists_as_deleted_keys, pin_bwd_block_lists_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -231,10 +289,13 @@ MUTANTS = {
     "empty_row_lse_zero": ("L = np.full(Lq, -np.inf)", "L = np.zeros(Lq)"),
     "packed_keys_from_query_offsets": ("K[h // G, ks:ke], V[h // G, ks:ke]", "K[h // G, qs:qe], V[h // G, qs:qe]"),
     "gqa_modulo": ("_attend(Q[b, h, r], K[b, h // G], V[b, h // G]", "_attend(Q[b, h, r], K[b, h % Hkv], V[b, h % Hkv]"),
-    "block_list_first_head_always": ("kl = hm[0] if len(hm) == 1 else hm[h]", "kl = hm[0]"),
+    "block_list_first_head_always": ("return hm[0] if len(hm) == 1 else hm[h]", "return hm[0]"),
     "bwd_without_jacobian_term": ("dS = P * (dP - Dr[:, None])", "dS = P * dP"),
     "bwd_dk_unscaled": ("dKb = scale * (dS.T @ Qb)", "dKb = dS.T @ Qb"),
-    "bwd_ignores_window": ("vis = visible(Qb.shape[0], Kb.shape[0], window)", "vis = visible(Qb.shape[0], Kb.shape[0])"),
+    "bwd_ignores_window": ("vis = visible(Qb.shape[0], Kb.shape[0], window, kl)",
+                           "vis = visible(Qb.shape[0], Kb.shape[0], kept_tiles=kl)"),
+    "bwd_ignores_block_lists": ("vis = visible(Qb.shape[0], Kb.shape[0], window, kl)",
+                                "vis = visible(Qb.shape[0], Kb.shape[0], window)"),
 }
 
 
