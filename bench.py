@@ -373,8 +373,9 @@ def bench_fp8(args):
 
 def bench_masks(args):
     """Mask-family forward: one JSON line for the N=8192 sliding-window workload in
-    TFLOP/s over the visible (query, key) pairs; the packed variable-length and the
-    block-sparse workloads are timed alongside (under `passes`)."""
+    TFLOP/s over the visible (query, key) pairs; its backward, and the forward and
+    backward of the packed variable-length and the block-sparse workloads, are timed
+    alongside (under `passes`)."""
     import numpy as np
     import torch
     import workloads
@@ -400,7 +401,17 @@ def bench_masks(args):
         pairs = sum(om.visible_pairs([lq], [lk], w.window, None if lists is None else [lists[b][0]])
                     for b, (lq, lk) in enumerate(zip(w.seqlens_q, w.seqlens_k)))
         flops = 4.0 * w.d * w.Hq * pairs
-        return run, flops, (q, k, v, cq, ck, lists)
+
+        def backward():
+            """The backward of the same problem (dO seeded), its workspace allocated once."""
+            run()
+            do = workloads.randn(w.seeds[0] + 50, tuple(qd.shape), qd.dtype).to(dev)
+            ws = torch.empty(fa.binding.load().fa_bwd_masked_workspace_size(w.B, w.Hq, w.Hkv, mq, mk, int(bi is not None)),
+                             dtype=torch.uint8, device=dev)
+            return lambda: fa.bwd_masked(qd, kd, vd, o, lse, do, w.window, w.scale, cqd, ckd, mq, mk, bc, bi,
+                                         workspace=ws)
+
+        return run, flops, (q, k, v, cq, ck, lists), backward
 
     nwarms = []
 
@@ -416,26 +427,25 @@ def bench_masks(args):
         return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
 
     w = workloads.MASK_WORKLOADS[args.workload or workloads.MASK_HEADLINE]
-    run, flops, cpu_inputs = prepare(w)
+    run, flops, cpu_inputs, backward = prepare(w)
     ms, wall_ms = timed(run, args.steps)
     achieved = flops / (ms * 1e-3) / 1e12
     passes = {}
-    if not w.packed and not w.block and not args.headline_only:
-        # the backward of the same masked problem (five products per visible pair)
-        qd, kd, vd = (t.to(dev) for t in cpu_inputs[:3])
-        do = workloads.randn(w.seeds[0] + 50, tuple(qd.shape), qd.dtype).to(dev)
-        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale)
-        ws = torch.empty(fa.binding.load().fa_bwd_masked_workspace_size(w.B, w.Hq, w.seqlens_q[0]),
-                         dtype=torch.uint8, device=dev)
-        mb, _ = timed(lambda: fa.bwd_masked(qd, kd, vd, o, lse, do, w.window, w.scale, workspace=ws), args.steps)
-        passes[w.name + " backward"] = {"ms": mb, "TFLOPs": 2.5 * flops / (mb * 1e-3) / 1e12,
-                                        "visible_pair_flops": 2.5 * flops}
+
+    def time_backward(name, backward, f):
+        # five products per visible pair against the forward's two
+        mb, _ = timed(backward(), args.steps)
+        passes[name + " backward"] = {"ms": mb, "TFLOPs": 2.5 * f / (mb * 1e-3) / 1e12, "visible_pair_flops": 2.5 * f}
+
+    if not args.headline_only:
+        time_backward(w.name, backward, flops)
     for name in workloads.MASK_WORKLOADS:
         if name == w.name or name.startswith("mix_") or args.headline_only:
             continue
-        r2, f2, _ = prepare(workloads.MASK_WORKLOADS[name])
+        r2, f2, _, b2 = prepare(workloads.MASK_WORKLOADS[name])
         m2, _ = timed(r2, args.steps)
         passes[name] = {"ms": m2, "TFLOPs": f2 / (m2 * 1e-3) / 1e12, "visible_pair_flops": f2}
+        time_backward(name, b2, f2)
     rec = {
         "metric": "mask-family attention forward TFLOPS (visible pairs) and % of the MFMA peak, sliding window at N=8192 d=128",
         "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": nwarms[0],

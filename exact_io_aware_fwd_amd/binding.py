@@ -62,10 +62,11 @@ def load() -> ctypes.CDLL:
     L.fa_fwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                 _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, ctypes.c_float, _vp]
     L.fa_fwd_masked.restype = ctypes.c_int
-    L.fa_bwd_masked_workspace_size.argtypes = [_i64, _i64, _i64]
+    L.fa_bwd_masked_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int]
     L.fa_bwd_masked_workspace_size.restype = ctypes.c_size_t
     L.fa_bwd_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64,
-                                _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float, _vp]
+                                _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64,
+                                ctypes.c_float, _vp]
     L.fa_bwd_masked.restype = ctypes.c_int
     L.fa_fp8_v_codes_bytes.argtypes = [_i64, _i64, _i64, _i64]
     L.fa_fp8_v_codes_bytes.restype = ctypes.c_size_t
@@ -373,6 +374,21 @@ def block_lists_to_tensors(lists, maxq: int, maxk: int, device):
     return cnt.to(device), idx.to(device)
 
 
+def _check_lists(block_cnt, block_idx, B: int, mq: int, mk: int, dev) -> int:
+    """Validate block-list tensors (as block_lists_to_tensors makes them); their head count."""
+    if (block_cnt is None) != (block_idx is None):
+        raise ValueError("give both block_cnt and block_idx, or neither")
+    if block_idx is None:
+        return 1
+    _check(block_cnt, "block_cnt", dev, torch.int32)
+    _check(block_idx, "block_idx", dev, torch.int32)
+    bh = block_idx.shape[1]
+    if block_cnt.dim() != 3 or block_idx.dim() != 4 or tuple(block_cnt.shape) != (B, bh, -(-mq // 256)) or \
+            block_idx.shape[:3] != block_cnt.shape or block_idx.shape[3] != max(-(-mk // 64), 1):
+        raise ValueError("block_cnt / block_idx have the wrong shape")
+    return bh
+
+
 def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, block_cnt=None, block_idx=None,
                out=None, lse=None):
@@ -410,14 +426,7 @@ def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_
         lse_shape = (B, Hq, Nq)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, dev, q.dtype)
-    bh = 1
-    if block_idx is not None:
-        _check(block_cnt, "block_cnt", dev, torch.int32)
-        _check(block_idx, "block_idx", dev, torch.int32)
-        bh = block_idx.shape[1]
-        if block_cnt.shape != (B, bh, -(-mq // 256)) or block_idx.shape[:3] != block_cnt.shape or \
-                block_idx.shape[3] < -(-mk // 64):
-            raise ValueError("block_cnt / block_idx have the wrong shape")
+    bh = _check_lists(block_cnt, block_idx, B, mq, mk, dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty(lse_shape, dtype=torch.float32, device=dev) if lse is None else lse
@@ -438,8 +447,9 @@ def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_
 
 def bwd_masked(q, k, v, o, lse, do, window=(-1, -1), softmax_scale: float | None = None, cu_seqlens_q=None,
                cu_seqlens_k=None, max_seqlen_q: int | None = None, max_seqlen_k: int | None = None,
-               workspace: torch.Tensor | None = None):
-    """dQ, dK, dV under the mask family via fa_bwd_masked (layouts as in fwd_masked)."""
+               block_cnt=None, block_idx=None, workspace: torch.Tensor | None = None):
+    """dQ, dK, dV under the mask family via fa_bwd_masked (layouts and block lists as in
+    fwd_masked)."""
     L = load()
     packed = cu_seqlens_q is not None
     dev = q.device
@@ -460,8 +470,9 @@ def bwd_masked(q, k, v, o, lse, do, window=(-1, -1), softmax_scale: float | None
     _check(lse, "lse", dev, torch.float32)
     if o.shape != q.shape or do.shape != q.shape or k.shape != v.shape:
         raise ValueError("o and do must match q; k and v must match")
+    bh = _check_lists(block_cnt, block_idx, B, mq, mk, dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    need = L.fa_bwd_masked_workspace_size(B, Hq, mq)
+    need = L.fa_bwd_masked_workspace_size(B, Hq, Hkv, mq, mk, int(block_idx is not None))
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if workspace is None else workspace
     dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
     ptr = lambda t: None if t is None else t.data_ptr()
@@ -470,7 +481,7 @@ def bwd_masked(q, k, v, o, lse, do, window=(-1, -1), softmax_scale: float | None
         st = L.fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Nq,
                              Nk, d, _dtype_code(q), ptr(cu_seqlens_q), ptr(cu_seqlens_k), mq, mk, int(window[0]),
-                             int(window[1]), scale, stream)
+                             int(window[1]), ptr(block_cnt), ptr(block_idx), bh, scale, stream)
     if st != FA_OK:
         _raise(st)
     return dq, dk, dv

@@ -204,6 +204,27 @@ fa_status check_masked(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t N
   return FA_OK;
 }
 
+// Block lists of the masked entry points (validated after check_masked has filled a):
+// both arrays or neither, block_heads 1 or Hq, 4-byte aligned unless there is no work.
+template <class Args>
+fa_status check_lists(const int32_t* block_cnt, const int32_t* block_idx, int64_t block_heads, int64_t Hq,
+                      bool empty, Args& a) {
+  if ((block_cnt == nullptr) != (block_idx == nullptr))
+    return fail(FA_ERR_INVALID_ARGUMENT, "give both block_cnt and block_idx, or neither");
+  if (block_idx != nullptr && block_heads != 1 && block_heads != Hq)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_heads must be 1 or Hq (got %lld)", (long long)block_heads);
+  fa_status st = FA_OK;
+  if (!empty && block_idx != nullptr && ((st = check_ptr4(block_cnt, "block_cnt")) != FA_OK ||
+                                         (st = check_ptr4(block_idx, "block_idx")) != FA_OK))
+    return st;
+  a.bcnt = block_cnt;
+  a.bidx = block_idx;
+  a.bheads = block_idx ? (int)block_heads : 1;
+  a.bnq = (a.maxq + 255) / 256;
+  a.bcap = (a.maxk + 63) / 64;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,49 +414,46 @@ fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, fl
   fa_status st = check_masked(B, Hq, Hkv, Nq, Nk, d, dtype, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                               window_left, window_right, softmax_scale, &empty, a);
   if (st != FA_OK) return st;
-  if ((block_cnt == nullptr) != (block_idx == nullptr))
-    return fail(FA_ERR_INVALID_ARGUMENT, "give both block_cnt and block_idx, or neither");
-  if (block_idx != nullptr && block_heads != 1 && block_heads != Hq)
-    return fail(FA_ERR_INVALID_ARGUMENT, "block_heads must be 1 or Hq (got %lld)", (long long)block_heads);
-  if (empty) return FA_OK;
+  if ((st = check_lists(block_cnt, block_idx, block_heads, Hq, empty, a)) != FA_OK || empty) return st;
   if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK)
     return st;
   if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK)) return st;
-  if (block_idx != nullptr && ((st = check_ptr4(block_cnt, "block_cnt")) != FA_OK ||
-                               (st = check_ptr4(block_idx, "block_idx")) != FA_OK))
-    return st;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.lse = lse;
-  a.bcnt = block_cnt;
-  a.bidx = block_idx;
-  a.bheads = block_idx ? (int)block_heads : 1;
-  a.bnq = (a.maxq + 255) / 256;
-  a.bcap = (a.maxk + 63) / 64;
   const hipError_t err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "masked forward launch failed: %s", hipGetErrorString(err));
   return FA_OK;
 }
 
-size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t max_seqlen_q) {
-  if (B < 0 || Hq < 0 || max_seqlen_q < 0) return 0;
-  return fa::bwd_rowterm_bytes(B, Hq, max_seqlen_q);
+size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                    int block_lists) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return 0;
+  size_t n = fa::bwd_rowterm_bytes(B, Hq, max_seqlen_q);
+  if (block_lists) n += fa::bwd_runs_bytes(B, Hq, Hkv, max_seqlen_q, max_seqlen_k);
+  return n;
 }
 
 fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t max_seqlen_q,
-                        int64_t max_seqlen_k, int64_t window_left, int64_t window_right, float softmax_scale,
+                        int64_t max_seqlen_k, int64_t window_left, int64_t window_right, const int32_t* block_cnt,
+                        const int32_t* block_idx, int64_t block_heads, float softmax_scale,
                         struct ihipStream_t* stream) {
   g_last_error[0] = '\0';
   bool empty = false;
   fa::BwdArgs a;
   fa_status st = check_masked(B, Hq, Hkv, Nq, Nk, d, dtype, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                               window_left, window_right, softmax_scale, &empty, a);
-  if (st != FA_OK || empty) return st;
+  if (st != FA_OK) return st;
+  if ((st = check_lists(block_cnt, block_idx, block_heads, Hq, empty, a)) != FA_OK || empty) return st;
+  const bool lists = block_idx != nullptr;
+  // run records: two ints per (query head of a group, 256-query block), G below 2^20
+  if (lists && (Hq / Hkv >= (1 << 20) || fa::bwd_runs_stride(Hq, Hkv, a.maxq) >= (1LL << 30)))
+    return fail(FA_ERR_UNSUPPORTED, "block lists: Hq/Hkv * ceil(max_seqlen_q/256) too large for the backward");
   if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK || (st = check_ptr(lse, "lse")) != FA_OK ||
       (st = check_ptr(dout, "dout")) != FA_OK || (st = check_ptr(dq, "dq")) != FA_OK ||
       (st = check_ptr(workspace, "workspace")) != FA_OK)
@@ -443,9 +461,14 @@ fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void*
   if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK ||
                  (st = check_ptr(dk, "dk")) != FA_OK || (st = check_ptr(dv, "dv")) != FA_OK))
     return st;
-  const size_t need = fa::bwd_rowterm_bytes(B, Hq, a.maxq);
+  const size_t rt = fa::bwd_rowterm_bytes(B, Hq, a.maxq);
+  const size_t need = rt + (lists ? fa::bwd_runs_bytes(B, Hq, Hkv, a.maxq, a.maxk) : 0);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if (lists) {
+    a.runs = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + rt);
+    a.rstride = fa::bwd_runs_stride(Hq, Hkv, a.maxq);
+  }
   a.q = q;
   a.k = k;
   a.v = v;

@@ -89,6 +89,102 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
   }
 }
 
+// Mask family: sequence b's query and key counts and first rows (0 with fixed lengths);
+// offsets are clamped to the tensors.
+__device__ __forceinline__ void seq_geometry(const BwdArgs& a, int b, int& Lq, int& Lk, int& qs, int& ks) {
+  Lq = a.N;
+  Lk = a.Nk;
+  qs = ks = 0;
+  if (a.cu_q != nullptr) {
+    qs = min(max(a.cu_q[b], 0), a.N);
+    const int qe = min(max(a.cu_q[b + 1], qs), a.N);
+    ks = min(max(a.cu_k[b], 0), a.Nk);
+    const int ke = min(max(a.cu_k[b + 1], ks), a.Nk);
+    Lq = min(qe - qs, a.maxq);
+    Lk = min(ke - ks, a.maxk);
+  }
+}
+
+// Mask family, dK/dV pass: the 32-query steps [qlo, qtop] (multiples of 32) that hold
+// every query whose window meets keys [k0, min(k0 + 128, Lk)); false if no query does.
+__device__ __forceinline__ bool dkdv_query_range(const BwdArgs& a, int Lq, int Lk, int k0, int& qlo, int& qtop) {
+  const int off = Lk - Lq;   // query i sits at key position i + off
+  const int kmax = min(k0 + 128, Lk) - 1;
+  const int iq_lo = a.wr >= 0 ? max(k0 - a.wr - off, 0) : 0;
+  const int iq_hi = a.wl >= 0 ? min(kmax + a.wl - off, Lq - 1) : Lq - 1;
+  qtop = iq_hi >= 0 ? iq_hi / 32 * 32 : 0;
+  qlo = iq_lo / 32 * 32;
+  return iq_lo <= iq_hi;
+}
+
+// ---- block lists, transposed for the dK/dV pass ----------------------------------------
+// The lists name, per 256-query block, the 64-key tiles it sees; the dK/dV pass walks a
+// 128-key block's queries instead.  One wave per (batch, K/V head, 128-key block) writes
+// the runs of 32-query steps that block visits, in the pass's order (query heads of the
+// group ascending, query blocks descending): one run per (head, 256-query block) whose
+// list holds either of the key block's two tiles, clipped to the queries whose window
+// meets the key block.  Record (BwdArgs::rstride ints): [0] runs, [1] steps, then per run
+// {first (highest) step's query row, g | steps << 20 | tiles << 28}, tiles bit 0 / bit 1
+// = the first / second tile listed.  Ballots keep the order, so the result is the same
+// on every run.
+__global__ void __launch_bounds__(256) bwd_runs_kernel(const BwdArgs a, long long nrec, int nkb) {
+  const int lane = threadIdx.x & 63;
+  const long long rec = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rec >= nrec) return;
+  const int jb = (int)(rec % nkb);
+  const int grp = (int)(rec / nkb);
+  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  int Lq, Lk, qs, ks;
+  seq_geometry(a, b, Lq, Lk, qs, ks);
+  const int k0 = jb * 128, t0 = k0 / 64;
+  int qlo = 0, qtop = 0;
+  const bool any = k0 < Lk && dkdv_query_range(a, Lq, Lk, k0, qlo, qtop);
+  const int tiles_ok = k0 + 64 < Lk ? 3 : 1;   // the second tile only if it holds keys
+  const int nqb = a.bnq, nf = G * nqb;
+  int* const out = a.runs + rec * a.rstride;
+  int base = 0, steps = 0;
+  for (int f0 = 0; any && f0 < nf; f0 += 64) {
+    const int f = f0 + lane;
+    int tiles = 0, first = 0, nst = 0, g = 0;
+    if (f < nf) {
+      g = f / nqb;
+      const int qb = nqb - 1 - (f - g * nqb);
+      const int hi = min(qb * 256 + 224, qtop), lo = max(qb * 256, qlo);
+      if (lo <= hi) {
+        const int hm = a.bheads == 1 ? 0 : hkv * G + g;
+        const size_t row = ((size_t)b * a.bheads + hm) * a.bnq + qb;
+        const int cnt = min(max(a.bcnt[row], 0), a.bcap);
+        const int* lst = a.bidx + row * a.bcap;
+        int p = lower_bound_tiles(lst, cnt, t0);
+        if (p < cnt && lst[p] == t0) {
+          tiles = 1;
+          ++p;
+        }
+        if (p < cnt && lst[p] == t0 + 1) tiles |= 2;
+        tiles &= tiles_ok;
+        first = hi;
+        nst = (hi - lo) / 32 + 1;
+      }
+    }
+    const unsigned long long m = __ballot(tiles != 0);
+    const int pos = base + __popcll(m & ((1ull << lane) - 1));
+    if (tiles != 0) {
+      out[2 + 2 * pos] = first;
+      out[3 + 2 * pos] = g | (nst << 20) | (tiles << 28);
+    }
+    base += __popcll(m);
+    int s = tiles != 0 ? nst : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    steps += s;
+  }
+  if (lane == 0) {
+    out[0] = base;
+    out[1] = steps;
+  }
+}
+
 // ---- 3. dK, dV per key block ---------------------------------------------------------
 // Q rows and dO rows of one 32-query step (XOR-swizzled chunks: lane's 16 bytes of
 // tile load i land where soff[i] says) and the step's 256 bytes of row terms, from HBM
@@ -167,15 +263,12 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   int Lq = N, Lk = N;
   size_t kvhead, qrow0, hs = (size_t)N;
   if constexpr (GEN) {
+    int qs, ks;
+    seq_geometry(a, b, Lq, Lk, qs, ks);
     if (a.cu_q != nullptr) {
-      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
-      const int ks = min(max(a.cu_k[b], 0), a.Nk), ke = min(max(a.cu_k[b + 1], ks), a.Nk);
-      Lq = min(qe - qs, a.maxq);
-      Lk = min(ke - ks, a.maxk);
       kvhead = (size_t)hkv * (size_t)a.Nk + ks;
       qrow0 = (size_t)hkv * G * (size_t)N + qs;
     } else {
-      Lk = a.Nk;
       kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
       qrow0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
     }
@@ -206,16 +299,22 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 
   // Steps: for each query head of the group, query blocks from the last down to the
   // first one that meets these keys (the key block's own start when causal; under a
-  // window, the blocks of queries whose window meets the block's keys).
+  // window, the blocks of queries whose window meets the block's keys; with block lists,
+  // only the runs of steps the transposed lists name).
   const int nb32 = ((GEN ? a.maxq : N) + 31) / 32;
   int qtop, qlo, nsteps;
+  const int* runs = nullptr;
+  int nruns = 0;
   if constexpr (GEN) {
-    const int kmax = min(k0 + BKV, Lk) - 1;
-    const int iq_lo = a.wr >= 0 ? max(k0 - a.wr - off, 0) : 0;
-    const int iq_hi = a.wl >= 0 ? min(kmax + a.wl - off, Lq - 1) : Lq - 1;
-    qtop = iq_hi >= 0 ? iq_hi / BQ * BQ : 0;
-    qlo = iq_lo / BQ * BQ;
-    nsteps = iq_lo <= iq_hi ? G * ((qtop - qlo) / BQ + 1) : 0;
+    static_assert(BKV == 128 && BQ == 32, "dkdv_query_range and the runs assume these");
+    const bool any = dkdv_query_range(a, Lq, Lk, k0, qlo, qtop);
+    if (a.runs != nullptr) {
+      runs = a.runs + ((long long)grp * ((a.maxk + BKV - 1) / BKV) + jb) * a.rstride;
+      nruns = runs[0];
+      nsteps = runs[1];
+    } else {
+      nsteps = any ? G * ((qtop - qlo) / BQ + 1) : 0;
+    }
   } else {
     qtop = (nb32 - 1) * BQ;
     qlo = CAUSAL ? k0 : 0;
@@ -230,15 +329,38 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     const int row = (nn % TI) * RPI + lane / CH;
     soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
   }
-  const unsigned char* dq_h = (const unsigned char*)a.q + qrow0 * ROWB;
-  const unsigned char* dg_h = (const unsigned char*)a.dout + qrow0 * ROWB;
-  const float* dr_h = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
+  const unsigned char* const q_g = (const unsigned char*)a.q + qrow0 * ROWB;
+  const unsigned char* const g_g = (const unsigned char*)a.dout + qrow0 * ROWB;
+  const float* const r_g = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
+  const unsigned char* dq_h = q_g;
+  const unsigned char* dg_h = g_g;
+  const float* dr_h = r_g;
   const int hbytes = Lq * ROWB, rbytes = nb32 * 256;   // buffer ranges: rows past Lq read 0
   int dqb = qtop;   // query block of the next step to load
-  auto dma_next = [&](unsigned char* sl) __attribute__((always_inline)) {
+  // block lists: run dri of the records, steps left in it, its tiles
+  int dri = 0, dleft = 0, dtiles = 3;
+  auto load_run = [&](int r) __attribute__((always_inline)) {
+    dqb = runs[2 + 2 * r];
+    const int w = runs[3 + 2 * r];
+    const int g = w & 0xfffff;
+    dleft = (w >> 20) & 15;
+    dtiles = (w >> 28) & 3;
+    dq_h = q_g + g * hs * ROWB;
+    dg_h = g_g + g * hs * ROWB;
+    dr_h = r_g + (long long)g * nb32 * 64;
+  };
+  // GEN: the query block and tiles of the step loaded into each slot
+  int sqb[3], stiles[3];
+  auto dma_next = [&](unsigned char* sl, int si) __attribute__((always_inline)) {
     dkdv_dma<ROWB, TI, LI, NW, TB>(dq_h, dg_h, dr_h, hbytes, rbytes, dqb * ROWB, dqb * 8, wave, lane, soff, sl);
+    if constexpr (GEN) {
+      sqb[si] = dqb;
+      stiles[si] = dtiles;
+    }
     dqb -= BQ;
-    if (dqb < qlo) {
+    if (GEN && runs != nullptr) {
+      if (--dleft == 0 && ++dri < nruns) load_run(dri);
+    } else if (dqb < qlo) {
       dqb = qtop;
       dq_h += hs * ROWB;
       dg_h += hs * ROWB;
@@ -295,8 +417,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   //   dK^T += Q^T dS.
   // dP_{n+1} starts from -D, so dP - D comes out of the MFMA.  The products of a step
   // past the last are formed anyway from a valid slot and never used.
-  int cqb = qtop;   // query block of the current step
-  f32x16 l2n;       // LSE*log2e of the current step's rows
+  int cqb_plain = qtop;   // query block of the current step (GEN: recorded per slot)
+  f32x16 l2n;             // LSE*log2e of the current step's rows
   auto step = [&](auto Jc, int n, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
     constexpr int J = decltype(Jc)::value;
     unsigned char* const bc = slot(J % 3);
@@ -306,7 +428,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
       wait_loads();      // this wave's loads of step n+1 landed
       __syncthreads();   // everyone's; everyone is done with slot (n-1)%3
     }
-    if (n + 2 < nsteps) dma_next(bl);
+    if (n + 2 < nsteps) dma_next(bl, (J + 2) % 3);
     const f32x16 l2 = l2n;
     const f32x16 nd = rt16(bn, 128);
     u32x4 qa = rowrd(bn, 0), ga = rowrd(bn + TB, 0);
@@ -331,15 +453,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     }
     l2n = rt16(bn, 0);
     bool active, full;
+    int cqb;   // the step's first query
     if constexpr (GEN) {
+      cqb = sqb[J % 3];
       // wave-uniform: does any (query, key) pair of this step and wave meet, do all?
+      // (with block lists, only if the list names this wave's tile)
       const int qmax = min(cqb + BQ, Lq) - 1, kmax = min(kw + 32, Lk) - 1;
       const int vlo = a.wl >= 0 ? cqb + off - a.wl : 0;              // keys some query sees
       const int vhi = a.wr >= 0 ? qmax + off + a.wr : Lk - 1;
-      active = kw <= kmax && cqb <= qmax && max(vlo, kw) <= min(vhi, kmax);
+      active = kw <= kmax && cqb <= qmax && max(vlo, kw) <= min(vhi, kmax) && ((stiles[J % 3] >> (wave >> 1)) & 1);
       full = kw + 31 < Lk && cqb + BQ - 1 < Lq && (a.wl < 0 || qmax + off - a.wl <= kw) &&
              (a.wr < 0 || kw + 31 <= cqb + off + a.wr);
     } else {
+      cqb = cqb_plain;
       active = !CAUSAL || cqb >= kw;
       full = !CAUSAL || cqb != kw;
     }
@@ -386,13 +512,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    cqb -= BQ;
-    if (cqb < qlo) cqb = qtop;
+    if constexpr (!GEN) {
+      cqb_plain -= BQ;
+      if (cqb_plain < qlo) cqb_plain = qtop;
+    }
   };
 
   if (nsteps > 0) {
-    dma_next(slot0);
-    if (nsteps > 1) dma_next(slot1);
+    if (GEN && runs != nullptr) load_run(0);
+    dma_next(slot0, 0);
+    if (nsteps > 1) dma_next(slot1, 1);
   }
   wait_loads();
   __syncthreads();
@@ -536,9 +665,12 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   for (int i = 0; i < 16; ++i) ndv[i] = negd;
 
   const int nkv = (Lk + BC - 1) / BC;
-  // key tiles t_lo + j, j < ntile; under a window, masked head [0, JH), plain [JH, JT),
-  // masked tail [JT, ntile) (a tile's flag covers its own two units)
-  int ntile, t_lo = 0, JH = 0, JT = 0;
+  // Key tiles visited, in order: tile_of(j), j < ntile (the mask family: the tiles of the
+  // workgroup's key interval, filtered by its 256-query block's list when there is one);
+  // masked head [0, JH), plain [JH, JT), masked tail [JT, ntile) (a tile's flag covers
+  // its own two units)
+  int ntile, t_lo = 0, p0 = 0, JH = 0, JT = 0;
+  const int* lst = nullptr;
   int lo_q = 0, hi_q = Lk - 1, wlo = 0, whi;
   if constexpr (GEN) {
     const int qlast = min(q0 + BR, Lq) - 1;
@@ -551,20 +683,45 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     const int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
     t_lo = klo / BC;
     const int t_hi = (Lk <= 0 || khi < klo) ? t_lo : khi / BC + 1;
-    ntile = t_hi - t_lo;
-    const int P1 = min(max((max(lo_of(qlast), 0) + BC - 1) / BC - t_lo, 0), ntile);
-    const int P2 = min(max((hi_of(q0) + 1) / BC - t_lo, 0), ntile);
+    // tiles that need element masks: below the largest lower bound, or past the smallest
+    // upper bound (which includes the tile holding key Lk-1 when Lk is ragged)
+    const int tm_head = (max(lo_of(qlast), 0) + BC - 1) / BC;
+    const int tm_tail = (hi_of(q0) + 1) / BC;
+    int P1, P2;
+    if (a.bidx != nullptr) {
+      static_assert(256 % BR == 0, "a workgroup's queries lie in one 256-query block of the lists");
+      const int hm = a.bheads == 1 ? 0 : hq;
+      const size_t row = ((size_t)b * a.bheads + hm) * a.bnq + q0 / 256;
+      const int cnt = min(max(a.bcnt[row], 0), a.bcap);
+      lst = a.bidx + row * a.bcap;
+      p0 = lower_bound_tiles(lst, cnt, t_lo);
+      ntile = lower_bound_tiles(lst, cnt, t_hi) - p0;
+      P1 = lower_bound_tiles(lst, cnt, tm_head) - p0;
+      P2 = lower_bound_tiles(lst, cnt, tm_tail) - p0;
+    } else {
+      ntile = t_hi - t_lo;
+      P1 = tm_head - t_lo;
+      P2 = tm_tail - t_lo;
+    }
+    P1 = min(max(P1, 0), ntile);
+    P2 = min(max(P2, 0), ntile);
     JH = min(ntile, (P1 + 2) / 3 * 3);
     JT = max(JH, P2 / 3 * 3);
   } else {
     ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
     whi = CAUSAL ? min(qw, N - 1) : N - 1;
   }
+  // tile index of list position j
+  auto tile_of = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (!GEN) return j;
+    if (lst == nullptr) return t_lo + j;
+    return min(max(lst[p0 + j], t_lo), nkv - 1);
+  };
 
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
   auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
-    Tiles::load(Kg, Vg, Lk, GEN ? t_lo + t : t, wave, doff, sl);
+    Tiles::load(Kg, Vg, Lk, tile_of(t), wave, doff, sl);
   };
 
   // per-lane LDS offsets: K rows (swizzled) and V rows (A operands of S^T, dP^T), K
@@ -643,7 +800,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
         if constexpr (decltype(MASK)::value) {
           // keys k0 + 8(v/4) + 4hh + v%4 of this lane's column; a unit every query of the
           // wave sees whole needs nothing
-          const int k0 = (GEN ? t_lo * 2 + u : u) * 32;
+          const int k0 = GEN ? tile_of(u >> 1) * BC + 32 * (u & 1) : u * 32;
           if (!(k0 >= wlo && k0 + 31 <= whi)) {
             int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;
             if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
@@ -784,6 +941,12 @@ static hipError_t launch_bwd_masked_t(const BwdArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const long long nkb = (a.maxk + 127) / 128;
   if (nkb <= 0) return hipSuccess;
+  if (a.runs != nullptr) {
+    const long long nrec = (long long)a.B * a.Hkv * nkb;
+    hipLaunchKernelGGL(bwd_runs_kernel, dim3((unsigned)((nrec + 3) / 4)), dim3(256), 0, stream, a, nrec, (int)nkb);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, false, true>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();

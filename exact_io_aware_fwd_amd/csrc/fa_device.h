@@ -149,6 +149,17 @@ static __device__ __forceinline__ float half_sum(float x) {
 
 static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Smallest p in [0, n) with list[p] >= t (n if none); list ascending (block lists).
+static __device__ __forceinline__ int lower_bound_tiles(const int* list, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < t) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // s_waitcnt vmcnt(0): this wave's global and buffer loads (LDS DMA included) are done.
 // A workgroup barrier does not wait for them by itself; put this before the barrier
 // that publishes a tile loaded by several waves.  (The builtin, unlike inline asm, is

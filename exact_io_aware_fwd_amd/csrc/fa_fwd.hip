@@ -50,17 +50,6 @@
 
 namespace fa {
 
-// Smallest p in [0, n) with list[p] >= t (n if none); list ascending.
-static __device__ __forceinline__ int lower_bound_tiles(const int* list, int n, int t) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] < t) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // GEN = the mask family: per-sequence lengths (packed or fixed, queries and keys of
 // different lengths, bottom-right aligned), a window (left, right) and optional
 // block lists of key tiles; CAUSAL is then unused (causal is the window (-1, 0)).

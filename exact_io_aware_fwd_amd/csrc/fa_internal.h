@@ -49,6 +49,13 @@ struct BwdArgs {
   const int* cu_k = nullptr;
   int maxq = 0, maxk = 0;
   int wl = -1, wr = -1;
+  // Block lists as in FwdArgs, and their transpose for the dK/dV pass (workspace, after
+  // the row terms): per (batch, K/V head, 128-key block) a record of rstride ints.
+  const int* bcnt = nullptr;
+  const int* bidx = nullptr;
+  int bheads = 1, bnq = 0, bcap = 0;
+  int* runs = nullptr;
+  long long rstride = 0;
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
@@ -140,6 +147,14 @@ hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, f
 // multiple of 32 per head (256 bytes per 32-row block).
 inline size_t bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)(B * Hq * ((N + 31) / 32) * 256);
+}
+// Transposed block lists of the masked backward: per (batch, K/V head, 128-key block)
+// two header ints and two ints per (query head of the group, 256-query block).
+inline int64_t bwd_runs_stride(int64_t Hq, int64_t Hkv, int64_t maxq) {
+  return 2 + 2 * (Hq / Hkv) * ((maxq + 255) / 256);
+}
+inline size_t bwd_runs_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t maxq, int64_t maxk) {
+  return (size_t)(B * Hkv * ((maxk + 127) / 128) * bwd_runs_stride(Hq, Hkv, maxq) * 4);
 }
 
 }  // namespace fa

@@ -199,26 +199,35 @@ fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, fl
                         struct ihipStream_t* stream);
 
 /*
- * Backward pass under the mask family (no block lists): the gradients of the output of
- * fa_fwd_masked with the same lengths, layout and window.  "FlashAttention Primer",
+ * Backward pass under the mask family: the gradients of the output of fa_fwd_masked
+ * with the same lengths, layout, window and block lists.  "FlashAttention Primer",
  * section "Backward pass: recomputation instead of storage" (P recomputed from the saved
- * LSE), with the masking of fa_fwd_masked.
+ * LSE), with the masking of fa_fwd_masked; "Flash Attention" (wiki), section
+ * "Block-sparse FlashAttention" (tiles off the lists are skipped in both passes).
  *
  *   q, k, v, o, lse, dout   as given to / returned by fa_fwd_masked (o, dout, dq like q;
  *                           dk, dv like k); a row with LSE = -inf contributes nothing
  *   dq, dk, dv              outputs, `dtype`; keys no query sees get dK = dV = 0; rows
  *                           outside every sequence (packed gaps) are not written
- *   workspace               >= fa_bwd_masked_workspace_size(B, Hq, max query length)
- *                           bytes, 16-byte aligned (row terms per (sequence, head))
+ *   block_cnt, block_idx,   as in fa_fwd_masked (NULL, NULL: no lists)
+ *   block_heads
+ *   workspace               >= fa_bwd_masked_workspace_size(B, Hq, Hkv, max query length,
+ *                           max key length, lists given) bytes, 16-byte aligned: row
+ *                           terms per (sequence, head) and, with lists, their transpose
+ *                           per 128-key block (Hq/Hkv * ceil(maxq/256) below 2^29, else
+ *                           FA_ERR_UNSUPPORTED)
+ * fa_bwd_masked_workspace_size returns 0 for negative sizes or Hq not a multiple of Hkv.
  * Deterministic (no atomics); nothing is allocated.  Errors as in fa_fwd_masked.
  */
-size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t max_seqlen_q);
+size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                    int block_lists);
 
 fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t max_seqlen_q,
-                        int64_t max_seqlen_k, int64_t window_left, int64_t window_right, float softmax_scale,
+                        int64_t max_seqlen_k, int64_t window_left, int64_t window_right, const int32_t* block_cnt,
+                        const int32_t* block_idx, int64_t block_heads, float softmax_scale,
                         struct ihipStream_t* stream);
 
 /*

@@ -241,16 +241,22 @@ def test_fwd_masked_empty(L):
 
 
 def bwd_masked(L, ws_bytes=1 << 20, B=1, Hq=2, Hkv=1, Nq=100, Nk=120, d=128, dtype=1, cq=None, ck=None, mq=0, mk=0,
-               wl=-1, wr=-1, scale=0.125, **ptrs):
+               wl=-1, wr=-1, bcnt=None, bidx=None, bh=1, scale=0.125, **ptrs):
     p = {n: P for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws")}
     p.update(ptrs)
     return L.fa_bwd_masked(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"], p["ws"],
-                           ws_bytes, B, Hq, Hkv, Nq, Nk, d, dtype, cq, ck, mq, mk, wl, wr, scale, None)
+                           ws_bytes, B, Hq, Hkv, Nq, Nk, d, dtype, cq, ck, mq, mk, wl, wr, bcnt, bidx, bh, scale, None)
+
+
+# row terms of B=1, Hq=2, 100 queries: 2 heads x 4 blocks of 32 rows x 256 bytes
+_RT = 2 * 4 * 256
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(dq=None), INV), (dict(ws=None), INV), (dict(ws_bytes=64), INV), (dict(cq=P), INV), (dict(wl=-3), INV),
     (dict(cq=P, ck=P, mq=500, mk=10), INV), (dict(d=96), UNS), (dict(Hq=3, Hkv=2), INV), (dict(scale=0.0), INV),
+    (dict(bcnt=P), INV), (dict(bcnt=P, bidx=P, bh=3), INV), (dict(bcnt=P + 2, bidx=P), INV),
+    (dict(bcnt=P, bidx=P, ws_bytes=_RT), INV),
 ])
 def test_bwd_masked_rejects(L, kw, expect):
     assert bwd_masked(L, **kw) == expect
@@ -259,5 +265,8 @@ def test_bwd_masked_rejects(L, kw, expect):
 
 def test_bwd_masked_workspace_and_empty(L):
     # row terms per (sequence, head), padded to 32-row blocks: 256 bytes per block
-    assert L.fa_bwd_masked_workspace_size(3, 4, 100) == 3 * 4 * 4 * 256
+    assert L.fa_bwd_masked_workspace_size(3, 4, 2, 100, 300, 0) == 3 * 4 * 4 * 256
+    # with block lists, per (sequence, K/V head, 128-key block) 2 + 2 * (Hq/Hkv) * ceil(maxq/256) ints
+    assert L.fa_bwd_masked_workspace_size(3, 4, 2, 100, 300, 1) == 3 * 4 * 4 * 256 + 3 * 2 * 3 * (2 + 2 * 2 * 1) * 4
+    assert L.fa_bwd_masked_workspace_size(3, 4, 3, 100, 300, 1) == 0
     assert bwd_masked(L, B=0) == OK and bwd_masked(L, Nq=0) == OK

@@ -1,14 +1,17 @@
 """GPU parity of the mask-family backward (fa_bwd_masked) against the fp64 oracle in
 oracle/masks.py: unequal query/key lengths (bottom-right), sliding windows on one or both
-sides, packed variable-length batches with empty sequences, GQA, both dtypes and head
-sizes, and the full-size sliding-window and packed workloads on sampled heads.
+sides, packed variable-length batches with empty sequences, block-sparse tile lists
+(shared and per head, with windows, packed, empty lists), GQA, both dtypes and head
+sizes, and the full-size sliding-window, packed and block-sparse workloads on sampled
+heads.
 
 Tolerance as for the 16-bit backward (gpu_util): rel-L2 of dQ, dK, dV <= 1e-2 against
 the oracle's gradients (the kernel is fed its own forward's O and LSE).  Rows that see no
 key must get dQ = 0 exactly and keys no query sees dK = dV = 0 exactly.  Where an exact
 gradient is identically zero (a window of one key per query gives P = 1, hence dQ = 0),
 its norm is compared with ||dV_ref|| instead, as in the square backward tests at N = 1.
-Without a mask the result must equal fa_bwd bit for bit.
+Without a mask the result must equal fa_bwd bit for bit, and lists naming every tile
+must equal no lists bit for bit.
 """
 from __future__ import annotations
 
@@ -106,6 +109,100 @@ def test_bwd_masked_packed():
         _check_grads(grads, ref, empty_q, unseen_k, label=str(window))
 
 
+def _random_lists(seed, B, Hm, Lq, Lk, density):
+    g = np.random.Generator(np.random.PCG64(seed))
+    nqb, nkt = -(-Lq // 256), -(-Lk // 64)
+    return [[[sorted(int(t) for t in np.nonzero(g.random(nkt) < density)[0]) for _ in range(nqb)]
+             for _ in range(Hm)] for _ in range(B)]
+
+
+def _list_masks(lists, lq, lk, window, Hq, G):
+    """Per sequence and query head: rows that see no key; per K/V head: keys no query sees."""
+    empty_q, unseen_k = [], []
+    for b in range(len(lq)):
+        eq, uk = [], []
+        for h in range(Hq):
+            hm = lists[b][0] if len(lists[b]) == 1 else lists[b][h]
+            vis = om.visible(lq[b], lk[b], window, hm)
+            eq.append(~vis.any(axis=1))
+            uk.append(vis.any(axis=0))
+        empty_q.append(np.stack(eq))
+        unseen_k.append(np.stack([~np.any(uk[g * G:(g + 1) * G], axis=0) for g in range(Hq // G)]))
+    return empty_q, unseen_k
+
+
+@pytest.mark.parametrize("Hm,window,density,d,dt", [
+    (1, (-1, -1), 0.3, 128, torch.bfloat16), (4, (-1, 0), 0.5, 128, torch.bfloat16),
+    (4, (200, 100), 0.7, 64, torch.float16), (1, (-1, 0), 0.0, 128, torch.bfloat16),
+    (4, (-1, -1), 0.15, 64, torch.bfloat16)])
+def test_bwd_masked_block_lists(Hm, window, density, d, dt):
+    B, Hq, Hkv, Nq, Nk = 2, 4, 2, 1100, 900
+    G = Hq // Hkv
+    q, k, v = _rand(9670, (B, Hq, Nq, d), dt), _rand(9671, (B, Hkv, Nk, d), dt), _rand(9672, (B, Hkv, Nk, d), dt)
+    do = _rand(9673, (B, Hq, Nq, d), dt)
+    lists = _random_lists(9674 + Hm, B, Hm, Nq, Nk, density)
+    say(f"[bwd masked lists] Hm={Hm} window={window} density={density} d={d} {dt}")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    bc, bi = fa.block_lists_to_tensors(lists, Nq, Nk, "cuda:0")
+    o, lse = fa.fwd_masked(qd, kd, vd, window, block_cnt=bc, block_idx=bi)
+    grads = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, block_cnt=bc, block_idx=bi)
+    torch.cuda.synchronize()
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ref = om.attention_bwd_masked(q, k, v, do, scale, window=window, block_lists=lists)
+    eq, uk = _list_masks(lists, [Nq] * B, [Nk] * B, window, Hq, G)
+    empty_q = np.broadcast_to(np.stack(eq)[..., None], (B, Hq, Nq, d))
+    unseen_k = np.broadcast_to(np.stack(uk)[..., None], (B, Hkv, Nk, d))
+    _check_grads(grads, ref, empty_q, unseen_k)
+
+
+def test_bwd_masked_block_lists_packed():
+    lq, lk = [0, 1, 255, 256, 600, 5, 300], [3, 0, 255, 700, 600, 64, 130]
+    Hq, Hkv, d = 4, 2, 128
+    G = Hq // Hkv
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q, k, v = _rand(9680, (Hq, cq[-1], d)), _rand(9681, (Hkv, ck[-1], d)), _rand(9682, (Hkv, ck[-1], d))
+    do = _rand(9683, (Hq, cq[-1], d))
+    mq, mk = max(lq), max(lk)
+    g = np.random.Generator(np.random.PCG64(9684))     # per sequence, its own blocks and tiles
+    lists = [[[sorted(int(t) for t in np.nonzero(g.random(-(-lk[b] // 64)) < 0.5)[0])
+               for _ in range(-(-lq[b] // 256))] for _ in range(Hq)] for b in range(len(lq))]
+    scale = float(np.float32(1 / np.sqrt(d)))
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    bc, bi = fa.block_lists_to_tensors(lists, mq, mk, "cuda:0")
+    for window in ((-1, -1), (-1, 0), (100, 20)):
+        say(f"[bwd masked lists packed] window={window}")
+        o, lse = fa.fwd_masked(qd, kd, vd, window, scale, cqd, ckd, mq, mk, bc, bi)
+        grads = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, scale, cqd, ckd, mq, mk, bc, bi)
+        torch.cuda.synchronize()
+        ref = om.attention_bwd_masked(q, k, v, do, scale, cq, ck, window, lists)
+        eq, uk = _list_masks(lists, lq, lk, window, Hq, G)
+        empty_q = np.zeros((Hq, cq[-1], d), dtype=bool)
+        unseen_k = np.zeros((Hkv, ck[-1], d), dtype=bool)
+        for b in range(len(lq)):
+            empty_q[:, cq[b]:cq[b + 1]] = eq[b][..., None]
+            unseen_k[:, ck[b]:ck[b + 1]] = uk[b][..., None]
+        _check_grads(grads, ref, empty_q, unseen_k, label=str(window))
+
+
+def test_bwd_masked_all_tiles_listed_equals_no_lists():
+    B, Hq, Hkv, N, d = 1, 4, 2, 1000, 128
+    q, k, v, do = (_rand(9690 + i, (B, Hq if i in (0, 3) else Hkv, N, d)) for i in range(4))
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    lists = [[[list(range(-(-N // 64))) for _ in range(-(-N // 256))]]]
+    bc, bi = fa.block_lists_to_tensors(lists, N, N, "cuda:0")
+    say("[bwd masked lists] every tile listed equals no lists, bit for bit; two calls agree")
+    for window in ((-1, -1), (300, 0)):
+        o, lse = fa.fwd_masked(qd, kd, vd, window)
+        g1 = fa.bwd_masked(qd, kd, vd, o, lse, dod, window)
+        g2 = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, block_cnt=bc, block_idx=bi)
+        g3 = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, block_cnt=bc, block_idx=bi)
+        torch.cuda.synchronize()
+        for a, b, c in zip(g1, g2, g3):
+            assert torch.equal(a, b) and torch.equal(b, c)
+
+
 def test_bwd_masked_equals_bwd_bitwise():
     q, k, v, do = to_dev(_rand(9660, (1, 8, 1000, 128)), _rand(9661, (1, 2, 1000, 128)), _rand(9662, (1, 2, 1000, 128)),
                          _rand(9663, (1, 8, 1000, 128)))
@@ -119,36 +216,40 @@ def test_bwd_masked_equals_bwd_bitwise():
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", [workloads.MASK_HEADLINE, "varlen_b8_hq32_hkv8_d128_bf16_causal"])
+@pytest.mark.parametrize("name", [workloads.MASK_HEADLINE, "varlen_b8_hq32_hkv8_d128_bf16_causal",
+                                  "bsparse_b1_hq16_hkv4_n8192_d128_bf16"])
 def test_bwd_mask_workloads_full_size_sampled_heads(name):
     """The full-size sliding-window and packed workloads (dO seeded), the oracle on two
     sampled query heads each with its K/V head; dK/dV of a K/V head sum over its query
     heads, so the oracle runs every query head of that group and the kernel's dK/dV are
     compared for those K/V heads."""
     w = workloads.MASK_WORKLOADS[name]
-    q, k, v, cq, ck, _ = workloads.make_mask_inputs(w)
+    q, k, v, cq, ck, lists = workloads.make_mask_inputs(w)
     do = _rand(w.seeds[0] + 50, tuple(q.shape))
     say(f"[bwd masked] {w.name} full size, sampled heads")
     qd, kd, vd, dod = to_dev(q, k, v, do)
     G = w.Hq // w.Hkv
+    mq, mk = max(w.seqlens_q), max(w.seqlens_k)
+    bc, bi = fa.block_lists_to_tensors(lists, mq, mk, "cuda:0") if lists is not None else (None, None)
     if w.packed:
-        mq, mk = max(w.seqlens_q), max(w.seqlens_k)
         cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
-        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale, cqd, ckd, mq, mk)
-        dq, dk, dv = fa.bwd_masked(qd, kd, vd, o, lse, dod, w.window, w.scale, cqd, ckd, mq, mk)
+        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale, cqd, ckd, mq, mk, bc, bi)
+        dq, dk, dv = fa.bwd_masked(qd, kd, vd, o, lse, dod, w.window, w.scale, cqd, ckd, mq, mk, bc, bi)
     else:
-        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale)
-        dq, dk, dv = fa.bwd_masked(qd, kd, vd, o, lse, dod, w.window, w.scale)
+        o, lse = fa.fwd_masked(qd, kd, vd, w.window, w.scale, block_cnt=bc, block_idx=bi)
+        dq, dk, dv = fa.bwd_masked(qd, kd, vd, o, lse, dod, w.window, w.scale, block_cnt=bc, block_idx=bi)
     torch.cuda.synchronize()
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     for hk in (0, w.Hkv - 1):
         hs = slice(hk * G, (hk + 1) * G)
+        sub = None if lists is None else [lb if len(lb) == 1 else lb[hs] for lb in lists]
         if w.packed:
-            ref = om.attention_bwd_masked(q[hs], k[hk:hk + 1], v[hk:hk + 1], do[hs], w.scale, cq, ck, w.window)
+            ref = om.attention_bwd_masked(q[hs], k[hk:hk + 1], v[hk:hk + 1], do[hs], w.scale, cq, ck, w.window,
+                                          sub)
             got = (dq[hs], dk[hk:hk + 1], dv[hk:hk + 1])
         else:
             ref = om.attention_bwd_masked(q[:1, hs], k[:1, hk:hk + 1], v[:1, hk:hk + 1], do[:1, hs], w.scale,
-                                          window=w.window)
+                                          window=w.window, block_lists=sub)
             got = (dq[:1, hs], dk[:1, hk:hk + 1], dv[:1, hk:hk + 1])
         for n, g, r in zip(("dQ", "dK", "dV"), got, ref):
             e = rel_l2(g.float().double().numpy(), r)
