@@ -431,9 +431,8 @@ fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, fl
 size_t fa_bwd_masked_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen_q, int64_t max_seqlen_k,
                                     int block_lists) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return 0;
-  size_t n = fa::bwd_rowterm_bytes(B, Hq, max_seqlen_q);
-  if (block_lists) n += fa::bwd_runs_bytes(B, Hq, Hkv, max_seqlen_q, max_seqlen_k);
-  return n;
+  if (block_lists) return fa::bwd_list_layout(B, Hq, Hkv, max_seqlen_q, max_seqlen_k).end;
+  return fa::bwd_rowterm_bytes(B, Hq, max_seqlen_q);
 }
 
 fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -461,13 +460,17 @@ fa_status fa_bwd_masked(const void* q, const void* k, const void* v, const void*
   if (Nk > 0 && ((st = check_ptr(k, "k")) != FA_OK || (st = check_ptr(v, "v")) != FA_OK ||
                  (st = check_ptr(dk, "dk")) != FA_OK || (st = check_ptr(dv, "dv")) != FA_OK))
     return st;
-  const size_t rt = fa::bwd_rowterm_bytes(B, Hq, a.maxq);
-  const size_t need = rt + (lists ? fa::bwd_runs_bytes(B, Hq, Hkv, a.maxq, a.maxk) : 0);
+  const fa::BwdListLayout lay = fa::bwd_list_layout(B, Hq, Hkv, a.maxq, a.maxk);
+  const size_t need = lists ? lay.end : fa::bwd_rowterm_bytes(B, Hq, a.maxq);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
   if (lists) {
-    a.runs = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + rt);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.runs = reinterpret_cast<int*>(ws + lay.runs);
     a.rstride = fa::bwd_runs_stride(Hq, Hkv, a.maxq);
+    a.plan = reinterpret_cast<int*>(ws + lay.plan);
+    a.table = reinterpret_cast<int*>(ws + lay.table);
+    a.pool = reinterpret_cast<float*>(ws + lay.pool);
   }
   a.q = q;
   a.k = k;

@@ -124,9 +124,9 @@ __device__ __forceinline__ bool dkdv_query_range(const BwdArgs& a, int Lq, int L
 // group ascending, query blocks descending): one run per (head, 256-query block) whose
 // list holds either of the key block's two tiles, clipped to the queries whose window
 // meets the key block.  Record (BwdArgs::rstride ints): [0] runs, [1] steps, then per run
-// {first (highest) step's query row, g | steps << 20 | tiles << 28}, tiles bit 0 / bit 1
-// = the first / second tile listed.  Ballots keep the order, so the result is the same
-// on every run.
+// {first (highest) step's query row, g | steps << 20 | tiles << 28, steps before it},
+// tiles bit 0 / bit 1 = the first / second tile listed.  Ballots and lane scans keep the
+// order, so the result is the same on every run.
 __global__ void __launch_bounds__(256) bwd_runs_kernel(const BwdArgs a, long long nrec, int nkb) {
   const int lane = threadIdx.x & 63;
   const long long rec = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -169,20 +169,112 @@ __global__ void __launch_bounds__(256) bwd_runs_kernel(const BwdArgs a, long lon
     }
     const unsigned long long m = __ballot(tiles != 0);
     const int pos = base + __popcll(m & ((1ull << lane) - 1));
+    const int s = tiles != 0 ? nst : 0;
+    int incl = s;   // steps of the kept runs of lanes 0 .. lane
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
     if (tiles != 0) {
-      out[2 + 2 * pos] = first;
-      out[3 + 2 * pos] = g | (nst << 20) | (tiles << 28);
+      out[2 + 3 * pos] = first;
+      out[3 + 3 * pos] = g | (nst << 20) | (tiles << 28);
+      out[4 + 3 * pos] = steps + incl - s;
     }
     base += __popcll(m);
-    int s = tiles != 0 ? nst : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    steps += s;
+    steps += __shfl(incl, 63);
   }
   if (lane == 0) {
     out[0] = base;
     out[1] = steps;
   }
+}
+
+// Sum, exclusive prefix sum and maximum over a workgroup of 1024 threads (16 waves), in a
+// fixed order; sh holds 16 entries.
+template <class T>
+__device__ __forceinline__ T wg1024_sum(T v, T* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T t = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+__device__ __forceinline__ int wg1024_excl_scan(int v, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += sh[i];
+  __syncthreads();
+  return off + incl - v;
+}
+__device__ __forceinline__ int wg1024_max(int v, int* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = sh[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) t = max(t, sh[i]);
+  __syncthreads();
+  return t;
+}
+
+// ---- chunk plan of the transposed lists (one workgroup) ---------------------------------
+// Chunk size C = max(kBwdMinChunk, ceil(total steps / kBwdTargetChunks)).  In record
+// order, a key block with more than C steps gets ceil(steps / C) chunks and as many
+// partial slots while the kBwdSlots last; the rest run whole.  plan[2r] = chunks of record
+// r, plan[2r+1] = its first slot; table[0] = slots used, table[1+2s], table[2+2s] = the
+// record and chunk of slot s.  Thread t takes a contiguous range of records, so one
+// prefix sum orders all of them; the same lists give the same plan.
+__global__ void __launch_bounds__(1024) bwd_plan_kernel(const BwdArgs a, int nrec) {
+  __shared__ long long shl[16];
+  __shared__ int shi[16];
+  const int t = threadIdx.x;
+  const int per = (nrec + 1023) / 1024;
+  const int r0 = min(t * per, nrec), r1 = min(r0 + per, nrec);
+  auto steps_of = [&](int r) { return a.runs[(long long)r * a.rstride + 1]; };
+  long long mine = 0;
+  for (int r = r0; r < r1; ++r) mine += steps_of(r);
+  const long long total = wg1024_sum(mine, shl);
+  const long long cl = (total + kBwdTargetChunks - 1) / kBwdTargetChunks;
+  const int C = (int)max((long long)kBwdMinChunk, cl);
+  auto chunks_of = [&](int st) { return st > C ? (st + C - 1) / C : 1; };
+  int want = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int n = chunks_of(steps_of(r));
+    want += n > 1 ? n : 0;
+  }
+  int pos = wg1024_excl_scan(want, shi);
+  int used = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int n = chunks_of(steps_of(r));
+    const int w = n > 1 ? n : 0;
+    const bool granted = w > 0 && pos + w <= kBwdSlots;
+    a.plan[2 * r] = granted ? n : 1;
+    a.plan[2 * r + 1] = granted ? pos : 0;
+    if (granted) {
+      for (int c = 0; c < n; ++c) {
+        a.table[1 + 2 * (pos + c)] = r;
+        a.table[2 + 2 * (pos + c)] = c;
+      }
+      used = pos + w;
+    }
+    pos += w;
+  }
+  used = wg1024_max(used, shi);
+  if (t == 0) a.table[0] = used;
 }
 
 // ---- 3. dK, dV per key block ---------------------------------------------------------
@@ -247,15 +339,35 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 
   // block -> (key block, batch, kv head): groups x, x+8, ... on XCD x (their Q/dO stay in
   // one L2), key blocks nearest the start (the most causal work) first
+  // With block lists, the first kBwdSlots blocks run the chunks of split key blocks (slot
+  // table; dealt round-robin over the XCDs and started first, being the long ones), and the
+  // primary block of a split key block has nothing to do.
   const int ngroups = a.B * a.Hkv;
-  int jb, grp;
-  if ((ngroups & 7) == 0) {
-    const int x = blockIdx.x & 7, sidx = blockIdx.x >> 3, per = ngroups >> 3;
-    jb = sidx / per;
-    grp = x + 8 * (sidx - jb * per);
-  } else {
-    jb = blockIdx.x / ngroups;
-    grp = blockIdx.x - jb * ngroups;
+  const int nkbg = GEN ? (a.maxk + BKV - 1) / BKV : 0;
+  int bid = blockIdx.x;
+  int jb, grp, chunk = 0;
+  bool mapped = false;
+  if (GEN && a.plan != nullptr) {
+    if (bid < kBwdSlots) {
+      if (bid >= a.table[0]) return;
+      const int rec = a.table[1 + 2 * bid];
+      chunk = a.table[2 + 2 * bid];
+      grp = rec / nkbg;
+      jb = rec - grp * nkbg;
+      mapped = true;
+    }
+    bid -= kBwdSlots;   // a multiple of 8: the XCD of each primary block is unchanged
+  }
+  if (!mapped) {
+    if ((ngroups & 7) == 0) {
+      const int x = bid & 7, sidx = bid >> 3, per = ngroups >> 3;
+      jb = sidx / per;
+      grp = x + 8 * (sidx - jb * per);
+    } else {
+      jb = bid / ngroups;
+      grp = bid - jb * ngroups;
+    }
+    if (GEN && a.plan != nullptr && a.plan[2 * (grp * nkbg + jb)] > 1) return;
   }
   const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
   // sequence geometry: Lq queries, Lk keys; qrow0 = first Q row of query head hkv*G,
@@ -304,14 +416,31 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const int nb32 = ((GEN ? a.maxq : N) + 31) / 32;
   int qtop, qlo, nsteps;
   const int* runs = nullptr;
-  int nruns = 0;
+  int nruns = 0, run0 = 0, skip0 = 0;   // with lists: the chunk starts skip0 steps into run run0
+  int nchunk = 1, pslot = 0;            // chunks of this key block, this chunk's partial slot
   if constexpr (GEN) {
     static_assert(BKV == 128 && BQ == 32, "dkdv_query_range and the runs assume these");
     const bool any = dkdv_query_range(a, Lq, Lk, k0, qlo, qtop);
     if (a.runs != nullptr) {
-      runs = a.runs + ((long long)grp * ((a.maxk + BKV - 1) / BKV) + jb) * a.rstride;
+      const int rec = grp * nkbg + jb;
+      runs = a.runs + (long long)rec * a.rstride;
       nruns = runs[0];
-      nsteps = runs[1];
+      const int steps = runs[1];
+      nchunk = a.plan[2 * rec];
+      pslot = a.plan[2 * rec + 1] + chunk;
+      const int per = (steps + nchunk - 1) / nchunk;
+      const int s0 = min(chunk * per, steps);
+      nsteps = min(s0 + per, steps) - s0;
+      if (nsteps > 0) {   // the last run that starts at or before step s0
+        int lo = 0, hi = nruns - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (runs[4 + 3 * mid] <= s0) lo = mid;
+          else hi = mid - 1;
+        }
+        run0 = lo;
+        skip0 = s0 - runs[4 + 3 * lo];
+      }
     } else {
       nsteps = any ? G * ((qtop - qlo) / BQ + 1) : 0;
     }
@@ -340,8 +469,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   // block lists: run dri of the records, steps left in it, its tiles
   int dri = 0, dleft = 0, dtiles = 3;
   auto load_run = [&](int r) __attribute__((always_inline)) {
-    dqb = runs[2 + 2 * r];
-    const int w = runs[3 + 2 * r];
+    dqb = runs[2 + 3 * r];
+    const int w = runs[3 + 3 * r];
     const int g = w & 0xfffff;
     dleft = (w >> 20) & 15;
     dtiles = (w >> 28) & 3;
@@ -519,7 +648,12 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   if (nsteps > 0) {
-    if (GEN && runs != nullptr) load_run(0);
+    if (GEN && runs != nullptr) {
+      dri = run0;
+      load_run(run0);
+      dqb -= BQ * skip0;
+      dleft -= skip0;
+    }
     dma_next(slot0, 0);
     if (nsteps > 1) dma_next(slot1, 1);
   }
@@ -559,6 +693,21 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   acc_drain(dk);
   acc_drain(dv);
 
+  if (GEN && nchunk > 1) {
+    // one chunk of a split key block: fp32 partial dK^T (unscaled), dV^T as [key][d]
+    float* pk = a.pool + (size_t)pslot * 2 * BKV * D + (size_t)(32 * wave + r32) * D;
+    float* pv = pk + BKV * D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * e + 8 * g4 + 4 * hh;
+        *(f32x4*)(pk + d0) = f32x4{dk[e][4 * g4], dk[e][4 * g4 + 1], dk[e][4 * g4 + 2], dk[e][4 * g4 + 3]};
+        *(f32x4*)(pv + d0) = f32x4{dv[e][4 * g4], dv[e][4 * g4 + 1], dv[e][4 * g4 + 2], dv[e][4 * g4 + 3]};
+      }
+    return;
+  }
+
   // dK = scale * (dK^T)^T, dV = (dV^T)^T, rounded to the input dtype
   if (mykey < Lk) {
     unsigned char* dKg = (unsigned char*)a.dk + (kvhead + mykey) * ROWB;
@@ -575,6 +724,47 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
         *(u32x2*)(dKg + d0 * 2) = wk;
         *(u32x2*)(dVg + d0 * 2) = wv;
       }
+  }
+}
+
+// ---- sum of the partial dK, dV of split key blocks ----------------------------------------
+// One workgroup per slot: the slot of chunk c of a key block split n ways takes keys
+// [128c/n, 128(c+1)/n) of the block, sums the n partials (consecutive slots) in chunk
+// order and writes dK = scale * sum, dV = sum in the input dtype.
+template <class Tag, int D>
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
+  using E = Elt<Tag>;
+  constexpr int ROWB = D * 2;
+  if ((int)blockIdx.x >= a.table[0]) return;
+  const int c = a.table[2 + 2 * blockIdx.x];
+  const int sl = blockIdx.x - c;   // chunk 0's slot
+  const int rec = a.table[1 + 2 * blockIdx.x];
+  const int nkbg = (a.maxk + 127) / 128;
+  const int grp = rec / nkbg, jb = rec - grp * nkbg;
+  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
+  int Lq, Lk, qs, ks;
+  seq_geometry(a, b, Lq, Lk, qs, ks);
+  const size_t kvhead =
+      a.cu_q != nullptr ? (size_t)hkv * (size_t)a.Nk + ks : (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+  const int n = a.plan[2 * rec];
+  const int k0 = jb * 128;
+  const int key0 = 128 * c / n, nk = 128 * (c + 1) / n - key0;
+  for (int i = threadIdx.x; i < 2 * nk * (D / 8); i += 256) {
+    const int t = i / (nk * (D / 8));   // 0: dK, 1: dV
+    const int e8 = i - t * nk * (D / 8);
+    const int key = key0 + e8 / (D / 8), d0 = (e8 % (D / 8)) * 8;
+    if (k0 + key >= Lk) continue;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < n; ++c) {
+      const float* p = a.pool + ((size_t)(sl + c) * 2 + t) * 128 * D + (size_t)key * D + d0;
+      lo += *(const f32x4*)p;
+      hi += *(const f32x4*)(p + 4);
+    }
+    const float m = t == 0 ? a.scale : 1.f;
+    const u32x4 w = {E::pack(lo[0] * m, lo[1] * m), E::pack(lo[2] * m, lo[3] * m), E::pack(hi[0] * m, hi[1] * m),
+                     E::pack(hi[2] * m, hi[3] * m)};
+    unsigned char* out = (unsigned char*)(t == 0 ? a.dk : a.dv) + (kvhead + k0 + key) * ROWB + d0 * 2;
+    *(u32x4*)out = w;
   }
 }
 
@@ -941,14 +1131,21 @@ static hipError_t launch_bwd_masked_t(const BwdArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const long long nkb = (a.maxk + 127) / 128;
   if (nkb <= 0) return hipSuccess;
+  const long long nrec = (long long)a.B * a.Hkv * nkb;
   if (a.runs != nullptr) {
-    const long long nrec = (long long)a.B * a.Hkv * nkb;
     hipLaunchKernelGGL(bwd_runs_kernel, dim3((unsigned)((nrec + 3) / 4)), dim3(256), 0, stream, a, nrec, (int)nkb);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(1024), 0, stream, a, (int)nrec);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, false, true>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
-                     stream, a);
+  const long long extra = a.runs != nullptr ? kBwdSlots : 0;   // later chunks of split key blocks, first
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, false, true>), dim3((unsigned)(nrec + extra)), dim3(256), 0, stream,
+                     a);
+  err = hipGetLastError();
+  if (err != hipSuccess || a.runs == nullptr) return err;
+  hipLaunchKernelGGL((bwd_reduce_kernel<Tag, D>), dim3(kBwdSlots), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -49,13 +49,17 @@ struct BwdArgs {
   const int* cu_k = nullptr;
   int maxq = 0, maxk = 0;
   int wl = -1, wr = -1;
-  // Block lists as in FwdArgs, and their transpose for the dK/dV pass (workspace, after
-  // the row terms): per (batch, K/V head, 128-key block) a record of rstride ints.
+  // Block lists as in FwdArgs, and (workspace, after the row terms) their transpose for
+  // the dK/dV pass: per (batch, K/V head, 128-key block) a record of rstride ints; the
+  // chunk plan (per record: chunks, first slot); the slot table; the partial dK/dV slots.
   const int* bcnt = nullptr;
   const int* bidx = nullptr;
   int bheads = 1, bnq = 0, bcap = 0;
   int* runs = nullptr;
   long long rstride = 0;
+  int* plan = nullptr;
+  int* table = nullptr;
+  float* pool = nullptr;
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
@@ -148,13 +152,34 @@ hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, f
 inline size_t bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)(B * Hq * ((N + 31) / 32) * 256);
 }
-// Transposed block lists of the masked backward: per (batch, K/V head, 128-key block)
-// two header ints and two ints per (query head of the group, 256-query block).
+// Block lists in the masked backward.  The dK/dV pass splits a key block whose
+// transposed list names more query steps than its share (total steps / kBwdTargetChunks,
+// at least kBwdMinChunk) into chunks run by separate workgroups; each chunk writes fp32
+// partial dK, dV (128 keys x d <= 128, both tensors) into one of kBwdSlots slots, and a
+// reduction sums them in chunk order.
+constexpr int kBwdSlots = 512;
+constexpr int kBwdTargetChunks = 256;
+constexpr int kBwdMinChunk = 64;
+// per (batch, K/V head, 128-key block): two header ints and three ints per (query head of
+// the group, 256-query block)
 inline int64_t bwd_runs_stride(int64_t Hq, int64_t Hkv, int64_t maxq) {
-  return 2 + 2 * (Hq / Hkv) * ((maxq + 255) / 256);
+  return 2 + 3 * (Hq / Hkv) * ((maxq + 255) / 256);
 }
-inline size_t bwd_runs_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t maxq, int64_t maxk) {
-  return (size_t)(B * Hkv * ((maxk + 127) / 128) * bwd_runs_stride(Hq, Hkv, maxq) * 4);
+// Byte offsets of the regions of the masked backward's workspace with block lists (the
+// row terms come first); `end` is its size.
+struct BwdListLayout {
+  size_t runs, plan, table, pool, end;
+};
+inline BwdListLayout bwd_list_layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t maxq, int64_t maxk) {
+  auto align = [](int64_t x) { return (size_t)((x + 255) / 256 * 256); };
+  const int64_t nrec = B * Hkv * ((maxk + 127) / 128);
+  BwdListLayout L;
+  L.runs = bwd_rowterm_bytes(B, Hq, maxq);
+  L.plan = L.runs + align(nrec * bwd_runs_stride(Hq, Hkv, maxq) * 4);
+  L.table = L.plan + align(nrec * 2 * 4);
+  L.pool = L.table + align((1 + 2 * (int64_t)kBwdSlots) * 4);
+  L.end = L.pool + (size_t)kBwdSlots * 2 * 128 * 128 * 4;
+  return L;
 }
 
 }  // namespace fa

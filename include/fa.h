@@ -215,7 +215,9 @@ fa_status fa_fwd_masked(const void* q, const void* k, const void* v, void* o, fl
  *                           max key length, lists given) bytes, 16-byte aligned: row
  *                           terms per (sequence, head) and, with lists, their transpose
  *                           per 128-key block (Hq/Hkv * ceil(maxq/256) below 2^29, else
- *                           FA_ERR_UNSUPPORTED)
+ *                           FA_ERR_UNSUPPORTED) and 64 MiB of fp32 partial dK/dV for key
+ *                           blocks whose lists name many query blocks (split over several
+ *                           workgroups, summed in a fixed order)
  * fa_bwd_masked_workspace_size returns 0 for negative sizes or Hq not a multiple of Hkv.
  * Deterministic (no atomics); nothing is allocated.  Errors as in fa_fwd_masked.
  */

@@ -266,7 +266,12 @@ def test_bwd_masked_rejects(L, kw, expect):
 def test_bwd_masked_workspace_and_empty(L):
     # row terms per (sequence, head), padded to 32-row blocks: 256 bytes per block
     assert L.fa_bwd_masked_workspace_size(3, 4, 2, 100, 300, 0) == 3 * 4 * 4 * 256
-    # with block lists, per (sequence, K/V head, 128-key block) 2 + 2 * (Hq/Hkv) * ceil(maxq/256) ints
-    assert L.fa_bwd_masked_workspace_size(3, 4, 2, 100, 300, 1) == 3 * 4 * 4 * 256 + 3 * 2 * 3 * (2 + 2 * 2 * 1) * 4
+    # with block lists: per (sequence, K/V head, 128-key block) a record of 2 + 3 * (Hq/Hkv) *
+    # ceil(maxq/256) ints and a plan of 2 ints, a slot table of 1 + 2 * 512 ints, and 512 slots
+    # of 2 x 128 x 128 floats; each region rounded up to 256 bytes
+    up = lambda x: -(-x // 256) * 256
+    nrec = 3 * 2 * 3
+    assert L.fa_bwd_masked_workspace_size(3, 4, 2, 100, 300, 1) == \
+        3 * 4 * 4 * 256 + up(nrec * (2 + 3 * 2 * 1) * 4) + up(nrec * 8) + up((1 + 2 * 512) * 4) + 512 * 2 * 128 * 128 * 4
     assert L.fa_bwd_masked_workspace_size(3, 4, 3, 100, 300, 1) == 0
     assert bwd_masked(L, B=0) == OK and bwd_masked(L, Nq=0) == OK

@@ -186,6 +186,32 @@ def test_bwd_masked_block_lists_packed():
         _check_grads(grads, ref, empty_q, unseen_k, label=str(window))
 
 
+@pytest.mark.parametrize("d,dt,window", [(128, torch.bfloat16, (-1, -1)), (64, torch.float16, (-1, 0))])
+def test_bwd_masked_block_lists_split_key_blocks(d, dt, window):
+    """Lists with global columns (a band plus every 8th tile) give a few key blocks many more
+    query steps than the rest; those run as several chunks whose fp32 partials are summed in
+    a fixed order.  Parity with the oracle, and two calls agree bit for bit."""
+    B, Hq, Hkv, N = 1, 8, 2, 2100
+    G = Hq // Hkv
+    q, k, v, do = (_rand(9700 + i, (B, Hq if i in (0, 3) else Hkv, N, d), dt) for i in range(4))
+    lists = [[workloads.local_global_tiles(N, N, band=3, stride=8)]]
+    say(f"[bwd masked lists split] N={N} d={d} {dt} window={window}")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    bc, bi = fa.block_lists_to_tensors(lists, N, N, "cuda:0")
+    o, lse = fa.fwd_masked(qd, kd, vd, window, block_cnt=bc, block_idx=bi)
+    g1 = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, block_cnt=bc, block_idx=bi)
+    g2 = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, block_cnt=bc, block_idx=bi)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ref = om.attention_bwd_masked(q, k, v, do, scale, window=window, block_lists=lists)
+    eq, uk = _list_masks(lists, [N], [N], window, Hq, G)
+    empty_q = np.broadcast_to(np.stack(eq)[..., None], (B, Hq, N, d))
+    unseen_k = np.broadcast_to(np.stack(uk)[..., None], (B, Hkv, N, d))
+    _check_grads(g1, ref, empty_q, unseen_k)
+
+
 def test_bwd_masked_all_tiles_listed_equals_no_lists():
     B, Hq, Hkv, N, d = 1, 4, 2, 1000, 128
     q, k, v, do = (_rand(9690 + i, (B, Hq if i in (0, 3) else Hkv, N, d)) for i in range(4))
