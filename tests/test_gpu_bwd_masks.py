@@ -281,3 +281,23 @@ def test_bwd_mask_workloads_full_size_sampled_heads(name):
             e = rel_l2(g.float().double().numpy(), r)
             say(f"    K/V head {hk}: {n} rel-L2 {e:.2e}")
             assert e <= GRAD_TOL, f"{n} rel-L2 {e:.3e}"
+
+
+def test_bwd_masked_inconsistent_lists_stay_in_bounds():
+    """As for the forward: lists that break the contract give unspecified but finite
+    gradients and no invalid access (counts and tiles are clamped; the transpose only
+    compares list entries)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 700, 128
+    q, k, v, do = to_dev(_rand(9980, (B, Hq, N, d)), _rand(9981, (B, Hkv, N, d)), _rand(9982, (B, Hkv, N, d)),
+                         _rand(9983, (B, Hq, N, d)))
+    nqb, cap = -(-N // 256), -(-N // 64)
+    g = torch.Generator().manual_seed(9984)
+    cnt = torch.randint(-3, cap + 6, (B, Hq, nqb), generator=g, dtype=torch.int32).cuda()
+    idx = torch.randint(-10, 2 * cap, (B, Hq, nqb, cap), generator=g, dtype=torch.int32).cuda()
+    say("[bwd masked] inconsistent block lists")
+    for window in ((-1, -1), (200, 0)):
+        o, lse = fa.fwd_masked(q, k, v, window, block_cnt=cnt, block_idx=idx)
+        grads = fa.bwd_masked(q, k, v, o, lse, do, window, block_cnt=cnt, block_idx=idx)
+        torch.cuda.synchronize()
+        for t in grads:
+            assert torch.isfinite(t.float()).all()

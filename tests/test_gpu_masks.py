@@ -196,3 +196,20 @@ def test_mask_workloads_full_size_sampled_heads(name):
             O_ref, L_ref = om.attention_fwd_masked(q[:, h:h + 1], k[:, kh], v[:, kh], w.scale, window=w.window,
                                                    block_lists=lists)
             _compare(o[:, h:h + 1], lse[:, h:h + 1], O_ref, L_ref, q.dtype)
+
+
+def test_masked_inconsistent_lists_stay_in_bounds():
+    """Lists that break the contract (unsorted, repeated and out-of-range tiles, counts
+    below 0 or above the row length) give unspecified values but no invalid access: the
+    kernel clamps every count and tile; the output must be finite."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 700, 128
+    q, k, v = to_dev(_rand(9970, (B, Hq, N, d)), _rand(9971, (B, Hkv, N, d)), _rand(9972, (B, Hkv, N, d)))
+    nqb, cap = -(-N // 256), -(-N // 64)
+    g = torch.Generator().manual_seed(9973)
+    cnt = torch.randint(-3, cap + 6, (B, Hq, nqb), generator=g, dtype=torch.int32)
+    idx = torch.randint(-10, 2 * cap, (B, Hq, nqb, cap), generator=g, dtype=torch.int32)
+    say("[masked] inconsistent block lists")
+    o, lse = fa.fwd_masked(q, k, v, (-1, -1), block_cnt=cnt.cuda(), block_idx=idx.cuda())
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert not torch.isnan(lse).any()
