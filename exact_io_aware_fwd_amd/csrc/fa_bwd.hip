@@ -15,11 +15,15 @@
 // once more, needs no atomics and no fp32 dQ buffer, and is bitwise reproducible.
 //
 //  1. row terms: LSE_i * log2(e) and D_i = sum_k dO_ik O_ik in fp32, as pairs;
-//  2. dQ pass: one workgroup per (batch, head, 32*NW-query block), the forward's
-//     structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K (XOR-
-//     swizzled: read by rows and transposed), V tiles streamed through LDS;
+//  2. dQ pass: one workgroup of 8 waves per (batch, head, 256-query block), the
+//     forward's structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K
+//     (XOR-swizzled: read by rows and transposed), V tiles streamed through LDS;
 //     P = exp2(S*scale*log2e - LSE*log2e),
-//     dS = P * (dP - D) in registers, dQ^T += K^T dS^T (K read transposed);
+//     dS = P * (dP - D) in registers, dQ^T += K^T dS^T (K read transposed).  d = 64
+//     overlaps one unit's elementwise work with the next unit's products; at d = 128 a
+//     second unit of S, dP does not fit in the 256 registers of a wave at two waves
+//     per SIMD, so each wave takes one unit at a time and the other wave on its SIMD
+//     fills the gaps;
 //  3. dK/dV pass: one workgroup per (batch, K/V head, 128-key block); each of the
 //     4 waves owns 32 keys, holds their K and V in VGPRs and dK^T, dV^T in
 //     accumulators across all query heads of the group and all query blocks (from
@@ -769,7 +773,9 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
 }
 
 // ---- 2. dQ per query block -------------------------------------------------------------
-template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
+// PIPE: the next unit's products interleaved with this unit's elementwise work (two
+// units of S, dP live at once); otherwise one unit at a time.
+template <class Tag, int D, bool CAUSAL, int NW, bool PIPE, bool GEN = false>
 __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
@@ -1012,10 +1018,43 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     accumulate(slc, hc, pf);
   };
 
+  // Without PIPE: unit u's S^T, dP^T from half h of slot sl, then its dS (masked as in
+  // step) and dQ^T += K_u^T dS_u^T.
+  auto step1 = [&](auto MASK, int u, const unsigned char* sl, int h) __attribute__((always_inline)) {
+    u32x4 kf = krow(sl, h, 0), vf = vrow(sl, h, 0);
+    f32x16 s, dp;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const u32x4 kc = kf, vc = vf;
+      if (k + 1 < NS) {
+        kf = krow(sl, h, k + 1);
+        vf = vrow(sl, h, k + 1);
+      }
+      s = E::mma(kc, qf[k], k == 0 ? zero16() : s);
+      dp = E::mma(vc, df[k], k == 0 ? ndv : dp);
+    }
+    dsfrom(s, dp, 0, 16);
+    if constexpr (decltype(MASK)::value) {
+      const int k0 = GEN ? tile_of(u >> 1) * BC + 32 * (u & 1) : u * 32;
+      if (!(k0 >= wlo && k0 + 31 <= whi)) {
+        int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;
+        if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+        const int llo = lo_q - k0 - 4 * hh;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int o = 8 * (v >> 2) + (v & 3);
+          if (o >= lim || (GEN && o < llo)) s[v] = 0.f;
+        }
+      }
+    }
+    const u32x4 pf[2] = {pack(s, 0), pack(s, 1)};
+    accumulate(sl, h, pf);
+  };
+
   f32x16 sa, pa, sb, pb;
   // Tile j (slot T = j % 3): sync, load tile j+2, units 2j (S, dP in sa, pa) and 2j+1
-  // (in sb, pb).  The products of the unit after the last are formed from a valid slot
-  // and never used.
+  // (in sb, pb).  With PIPE, the products of the unit after the last are formed from a
+  // valid slot and never used.
   auto tile = [&](auto Tc, auto MASK, int j) __attribute__((always_inline)) {
     constexpr int T = decltype(Tc)::value;
     unsigned char* const sc = slot(T);
@@ -1025,8 +1064,13 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
       __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
     if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
-    step(MASK, 2 * j, sc, 0, sc, 1, sa, pa, sb, pb);
-    step(MASK, 2 * j + 1, sc, 1, sn, 0, sb, pb, sa, pa);
+    if constexpr (PIPE) {
+      step(MASK, 2 * j, sc, 0, sc, 1, sa, pa, sb, pb);
+      step(MASK, 2 * j + 1, sc, 1, sn, 0, sb, pb, sa, pa);
+    } else {
+      step1(MASK, 2 * j, sc, 0);
+      step1(MASK, 2 * j + 1, sc, 1);
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -1039,12 +1083,14 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   if (ntile > 1) dma(1, slot1);
   wait_loads();
   __syncthreads();
-  sa = zero16();
-  pa = ndv;
+  if constexpr (PIPE) {
+    sa = zero16();
+    pa = ndv;
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    sa = E::mma(krow(slot0, 0, st), qf[st], sa);
-    pa = E::mma(vrow(slot0, 0, st), df[st], pa);
+    for (int st = 0; st < NS; ++st) {
+      sa = E::mma(krow(slot0, 0, st), qf[st], sa);
+      pa = E::mma(vrow(slot0, 0, st), df[st], pa);
+    }
   }
   // Tiles whose units all precede every wave's last unit need no mask.
   if constexpr (!GEN) {
@@ -1100,12 +1146,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, a, prows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // d = 128: Q, dO, the dQ accumulator and two units of S, dP need more than the 256
-  // registers a wave has at two waves per SIMD, so that case runs 4 waves (1 per SIMD).
-  constexpr int NWQ = D == 128 ? 4 : 8;
+  // 8 waves (2 per SIMD); at d = 128 one unit at a time (see the dQ pass)
+  constexpr int NWQ = 8;
   const long long nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, NWQ>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(NWQ * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, NWQ, D != 128>), dim3((unsigned)(nqb * a.B * a.Hq)),
+                     dim3(NWQ * 64), 0, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long nkb = (a.N + 127) / 128;
@@ -1123,9 +1168,9 @@ static hipError_t launch_bwd_masked_t(const BwdArgs& a, hipStream_t stream) {
                      stream, a, prows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int NWQ = D == 128 ? 4 : 8;
+  constexpr int NWQ = 8;
   const long long nqb = (a.maxq + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, false, NWQ, true>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(NWQ * 64),
+  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, false, NWQ, D != 128, true>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(NWQ * 64),
                      0, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
