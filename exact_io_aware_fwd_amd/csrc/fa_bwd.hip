@@ -913,6 +913,14 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     if (lst == nullptr) return t_lo + j;
     return min(max(lst[p0 + j], t_lo), nkv - 1);
   };
+  // keys some query of this wave sees: [ulo, uhi] (empty when the wave has no query)
+  int ulo = 0, uhi;
+  if constexpr (GEN) {
+    ulo = max(a.wl >= 0 ? qw + off - a.wl : 0, 0);
+    uhi = qw >= Lq ? -1 : a.wr >= 0 ? min(min(qw + 31, Lq - 1) + off + a.wr, Lk - 1) : Lk - 1;
+  } else {
+    uhi = qw >= N ? -1 : CAUSAL ? min(qw + 31, N - 1) : N - 1;
+  }
 
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
@@ -1019,8 +1027,14 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   };
 
   // Without PIPE: unit u's S^T, dP^T from half h of slot sl, then its dS (masked as in
-  // step) and dQ^T += K_u^T dS_u^T.
+  // step) and dQ^T += K_u^T dS_u^T; in masked tiles a unit the wave cannot see is skipped.
   auto step1 = [&](auto MASK, int u, const unsigned char* sl, int h) __attribute__((always_inline)) {
+    if constexpr (decltype(MASK)::value) {
+      // a unit no query of this wave sees adds nothing: skip it (wave-uniform; the other
+      // wave on the SIMD takes the freed cycles)
+      const int k0 = GEN ? tile_of(u >> 1) * BC + 32 * (u & 1) : u * 32;
+      if (k0 > uhi || k0 + 31 < ulo) return;
+    }
     u32x4 kf = krow(sl, h, 0), vf = vrow(sl, h, 0);
     f32x16 s, dp;
 #pragma unroll
