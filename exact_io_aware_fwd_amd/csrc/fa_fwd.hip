@@ -455,8 +455,197 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   }
 }
 
+// The d = 128 forward without the mask family: 12 waves of 32 queries (three per SIMD),
+// each taking one 32-key unit at a time — scores, mask, reference max, exponentials and
+// row sum, then O^T += V^T P^T — with no software pipeline: the other waves on the SIMD
+// overlap one wave's softmax with their products.  Without the pipeline's second unit a
+// wave needs ~150 registers, which three waves per SIMD allow (two waves per SIMD with
+// the same code run slower than the pipelined kernel above; three run faster).  Same
+// tiles, loads, layouts, rescaling threshold and epilogue as fwd_kernel; a unit that no
+// query of a wave sees (past its diagonal) is skipped by that wave.
+template <class Tag, int D, bool CAUSAL>
+__global__ void __launch_bounds__(768) fwd_unit_kernel(const FwdArgs a) {
+  using E = Elt<Tag>;
+  constexpr int NW = 12;
+  constexpr int BR = 32 * NW;
+  constexpr int BC = 64;
+  constexpr int ROWB = D * 2;
+  constexpr int PK = ROWB + 16;
+  constexpr int PV = ROWB + 64;
+  using Tiles = TilePair<ROWB, PK, PV, NW>;
+  constexpr int KBYTES = Tiles::ABYTES;
+  constexpr int SLOT = Tiles::SLOT;
+  constexpr int IPW = Tiles::IPW;
+  constexpr int NE = D / 32;
+  constexpr int NS = D / 16;
+  constexpr float TAU = 8.f;
+  // three LDS slots as distinct objects, as in fwd_kernel
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5, r32 = lane & 31;
+  const int N = a.N;
+  int b, hq, iq;
+  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  const unsigned char* Qg = (const unsigned char*)a.q + qhead * ROWB;
+  const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
+  const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
+  const int q0 = iq * BR;
+  const int qw = q0 + wave * 32;
+  const int myq = qw + r32;
+  u32x4 qf[NS];
+  if (myq < N) {
+    const unsigned char* qp = Qg + (size_t)myq * ROWB + 16 * hh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qp + 32 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = u32x4{0, 0, 0, 0};
+  }
+  const int nkv = (N + BC - 1) / BC;
+  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+  const int uhi = qw >= N ? -1 : CAUSAL ? min(qw + 31, N - 1) : N - 1;   // keys some query sees
+  const int whi = CAUSAL ? min(qw, N - 1) : N - 1;                       // keys every query sees
+  // K rows (A operand of S^T) and V read transposed (A operand of O^T), as in fwd_kernel
+  int doff[IPW];
+  Tiles::offsets(wave, lane, doff);
+  const int ka = r32 * PK + 16 * hh;
+  const int va = KBYTES + (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  auto kread = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
+  };
+  auto vread = [&](const unsigned char* sl, int hv, int h, int e) __attribute__((always_inline)) {
+    const unsigned char* p = sl + hv * 32 * PV + va;
+    return cat(lds_read_tr(p + 16 * h * PV + 64 * e), lds_read_tr(p + (16 * h + 8) * PV + 64 * e));
+  };
+  const float c2 = a.scale_log2;
+  float mr = -INFINITY, l_run = 0.f;
+  f32x16 o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[e][v] = 0.f;
+  // unit u = keys 32u .. 32u+31, half h of the tile in slot sl
+  auto unit = [&](int u, const unsigned char* sl, int h) __attribute__((always_inline)) {
+    const int k0 = u * 32;
+    if (k0 > uhi) return;   // wave-uniform: no query of this wave sees these keys
+    f32x16 s;
+    u32x4 kf = kread(sl, h, 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const u32x4 kc = kf;
+      if (st + 1 < NS) kf = kread(sl, h, st + 1);
+      s = E::mma(kc, qf[st], st == 0 ? zero16() : s);
+    }
+    u32x4 vf = vread(sl, h, 0, 0);   // first PV operand, read while the scores settle
+    if (!(k0 + 31 <= whi)) {   // keys past N or (causal) after the query: -inf
+      int lim = N - k0 - 4 * hh;
+      if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int oo = 8 * (v >> 2) + (v & 3);
+        if (oo >= lim) s[v] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    mx = half_max(mx) * c2;
+    // the reference max moves only when a row's max passes it by TAU (log2 units)
+    const bool raise = mx > mr + TAU;
+    const float mnew = raise ? mx : mr;
+    const float alpha = (mr == -INFINITY) ? 0.f : fast_exp2(mr - mnew);
+    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+    mr = mnew;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s[v] = fast_exp2(fmaf(s[v], c2, -mref));
+      rs += s[v];
+    }
+    l_run = fmaf(l_run, alpha, rs);
+    const u32x4 pf[2] = {
+        u32x4{E::pack(s[0], s[1]), E::pack(s[2], s[3]), E::pack(s[4], s[5]), E::pack(s[6], s[7])},
+        u32x4{E::pack(s[8], s[9]), E::pack(s[10], s[11]), E::pack(s[12], s[13]), E::pack(s[14], s[15])}};
+#pragma unroll
+    for (int k = 0; k < 2 * NE; ++k) {
+      const int t = k / NE, e = k % NE;
+      const u32x4 vc = vf;
+      if (k + 1 < 2 * NE) vf = vread(sl, h, (k + 1) / NE, (k + 1) % NE);
+      o[e] = E::mma(vc, pf[t], o[e]);
+    }
+  };
+  auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
+    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+  };
+  // tile j in slot j % 3: sync, load tile j+2, its two units
+  auto tile = [&](auto Tc, int j) __attribute__((always_inline)) {
+    constexpr int T = decltype(Tc)::value;
+    unsigned char* const sc = slot(T);
+    if (j > 0) {
+      wait_loads();      // this wave's loads of tile j landed
+      __syncthreads();   // everyone's; slot (j-1)%3 is free
+    }
+    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    unit(2 * j, sc, 0);
+    unit(2 * j + 1, sc, 1);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  dma(0, slot0);
+  if (ntile > 1) dma(1, slot1);
+  wait_loads();
+  __syncthreads();
+  for (int j = 0; j < ntile; j += 3) {
+    tile(I0{}, j);
+    if (j + 1 >= ntile) break;
+    tile(I1{}, j + 1);
+    if (j + 2 >= ntile) break;
+    tile(I2{}, j + 2);
+  }
+  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
+  const float l_tot = half_sum(l_run);
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * e + 8 * g + 4 * hh;
+        const u32x2 w = {E::pack(o[e][4 * g + 0] * inv, o[e][4 * g + 1] * inv),
+                         E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
+        *(u32x2*)(Og + d0 * 2) = w;
+      }
+    if (hh == 0) a.lse[qhead + myq] = (mr + log2f(l_tot)) * kLn2;
+  }
+}
+
+
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128) {
+    constexpr int BRU = 32 * 12;
+    const long long nb = (long long)a.B * a.Hq * ((a.N + BRU - 1) / BRU);
+    if (nb <= 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL>), dim3((unsigned)nb), dim3(768), 0, stream, a);
+    return hipGetLastError();
+  }
   constexpr int BR = 256;
   const int nqb = (a.N + BR - 1) / BR;
   const long long nblocks = (long long)a.B * a.Hq * nqb;
