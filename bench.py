@@ -553,7 +553,7 @@ def main():
     peak = metrics.MFMA_BF16_TFLOPS
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
-    passes = {"fwd": {"kernel": "fwd_kernel", "launches": 1, "ms": fwd_ms,
+    passes = {"fwd": {"kernel": "fwd_unit_kernel", "launches": 1, "ms": fwd_ms,
                       "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12}}
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
     if not args.fwd_only:

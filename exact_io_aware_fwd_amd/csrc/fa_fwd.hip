@@ -12,9 +12,15 @@
 // tile follows the section "FlashAttention-3" (matmul/softmax interleaving),
 // realised here inside each wave's instruction stream.
 //
-// gfx950 design.
-//  * A workgroup owns 256 query rows, 8 waves x 32 rows; one workgroup per CU,
-//    two waves per SIMD.
+// gfx950 design.  Two kernels share tiles, layouts and arithmetic:
+//  * fwd_unit_kernel (fa_fwd): 12 waves x 32 query rows at d = 128 (three waves per
+//    SIMD), 16 at d = 64 (four); each wave takes one 32-key unit at a time and the
+//    other waves on its SIMD overlap its softmax with their products.
+//  * fwd_kernel (the mask family, fa_fwd_masked): 8 waves x 32 rows (256-row blocks,
+//    the granularity of the block lists), two waves per SIMD, with a software
+//    pipeline per wave: the products S_{u+1} = K_{u+1} Q^T are issued while the
+//    softmax of unit u runs, then O^T += V_u^T P_u; the two waves of a SIMD run half a
+//    unit apart.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: every
 //    lane holds the scores of ONE query (lane % 32) for 32 keys, so the row max
 //    and row sum are in-lane plus one permlane32 swap, and the probabilities are
@@ -31,14 +37,12 @@
 //    (measured free of bank conflicts), and every LDS address is a lane
 //    constant plus an immediate.  The loads use buffer descriptors that end at
 //    row N, so rows past the sequence end land as zeros.
-//  * Software pipeline per wave: the products S_{j+1} = K_{j+1} Q^T are issued
-//    while the softmax of tile j runs, then O^T += V_j^T P_j.
 //  * Scores are kept in log2 units.  The reference max is raised only when a
 //    row's max exceeds it by more than 8 (so P <= 256), and O is rescaled only
 //    when some lane of the wave raised it.
-//  * Causal: a workgroup stops at the last tile its rows can see.  Tiles before every
-//    wave's diagonal run unmasked; the few after run a masked variant in which a wave
-//    past its diagonal adds only zeros (no branches, so no register shuffling).
+//  * Causal: a workgroup stops at the last tile its rows can see; units no query of a
+//    wave sees are skipped by that wave (fwd_unit_kernel) or add only zeros in a
+//    masked variant without branches (fwd_kernel).
 //  * Block ids are remapped so that all query blocks sharing a K/V head run on
 //    one XCD (block ids are dealt round-robin over the 8 XCDs) and the longest
 //    causal blocks start first.
@@ -455,18 +459,18 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   }
 }
 
-// The d = 128 forward without the mask family: 12 waves of 32 queries (three per SIMD),
-// each taking one 32-key unit at a time — scores, mask, reference max, exponentials and
-// row sum, then O^T += V^T P^T — with no software pipeline: the other waves on the SIMD
-// overlap one wave's softmax with their products.  Without the pipeline's second unit a
-// wave needs ~150 registers, which three waves per SIMD allow (two waves per SIMD with
-// the same code run slower than the pipelined kernel above; three run faster).  Same
-// tiles, loads, layouts, rescaling threshold and epilogue as fwd_kernel; a unit that no
-// query of a wave sees (past its diagonal) is skipped by that wave.
-template <class Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__(768) fwd_unit_kernel(const FwdArgs a) {
+// The forward without the mask family: NW waves of 32 queries, each taking one 32-key
+// unit at a time — scores, mask, reference max, exponentials and row sum, then
+// O^T += V^T P^T — with no software pipeline: the other waves on the SIMD overlap one
+// wave's softmax with their products.  Without the pipeline's second unit a wave needs
+// ~150 registers at d = 128 (three waves per SIMD: NW = 12) and ~90 at d = 64 (four:
+// NW = 16); two waves per SIMD with the same code run slower than the pipelined kernel
+// above, three and four faster.  Same tiles, loads, layouts, rescaling threshold and
+// epilogue as fwd_kernel, and the same arithmetic in the same order; a unit that no
+// query of a wave sees (past its diagonal) is skipped by that wave, which changes no bit.
+template <class Tag, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
-  constexpr int NW = 12;
   constexpr int BR = 32 * NW;
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;
@@ -639,18 +643,11 @@ __global__ void __launch_bounds__(768) fwd_unit_kernel(const FwdArgs a) {
 
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 128) {
-    constexpr int BRU = 32 * 12;
-    const long long nb = (long long)a.B * a.Hq * ((a.N + BRU - 1) / BRU);
-    if (nb <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL>), dim3((unsigned)nb), dim3(768), 0, stream, a);
-    return hipGetLastError();
-  }
-  constexpr int BR = 256;
-  const int nqb = (a.N + BR - 1) / BR;
-  const long long nblocks = (long long)a.B * a.Hq * nqb;
-  if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)nblocks), dim3(512), 0, stream, a);
+  constexpr int NW = D == 128 ? 12 : 16;
+  constexpr int BR = 32 * NW;
+  const long long nb = (long long)a.B * a.Hq * ((a.N + BR - 1) / BR);
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, NW>), dim3((unsigned)nb), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
