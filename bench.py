@@ -457,7 +457,7 @@ def bench_masks(args):
         "passes": passes,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": metrics.MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / metrics.MFMA_BF16_TFLOPS, "traffic": traffic_bytes("masks"),
-                     "kernel": "fwd_kernel<bf16, 128, false, true>", "avg_ms": ms, "algorithmic_flops": flops},
+                     "kernel": "fwd_unit_kernel<bf16, 128, false, 12, true>", "avg_ms": ms, "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:
         try:

@@ -467,8 +467,10 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 // NW = 16); two waves per SIMD with the same code run slower than the pipelined kernel
 // above, three and four faster.  Same tiles, loads, layouts, rescaling threshold and
 // epilogue as fwd_kernel, and the same arithmetic in the same order; a unit that no
-// query of a wave sees (past its diagonal) is skipped by that wave, which changes no bit.
-template <class Tag, int D, bool CAUSAL, int NW>
+// query of a wave sees (past its diagonal, outside its window) is skipped by that
+// wave, which changes no bit.  GEN: the mask family without block lists (lengths,
+// packed batches, windows) as in fwd_kernel.
+template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
 __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
   constexpr int BR = 32 * NW;
@@ -495,18 +497,37 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
   int b, hq, iq;
-  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  map_q_block(((GEN ? a.maxq : N) + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
   const int hkv = hq / (a.Hq / a.Hkv);
-  const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  // sequence geometry: Lq queries, Lk keys (offsets clamped to the tensors)
+  int Lq = N, Lk = N;
+  size_t qhead, kvhead;
+  if constexpr (GEN) {
+    if (a.cu_q != nullptr) {
+      const int qs = min(max(a.cu_q[b], 0), N), qe = min(max(a.cu_q[b + 1], qs), N);
+      const int ks = min(max(a.cu_k[b], 0), a.Nk), ke = min(max(a.cu_k[b + 1], ks), a.Nk);
+      Lq = min(qe - qs, a.maxq);
+      Lk = min(ke - ks, a.maxk);
+      qhead = (size_t)hq * (size_t)N + qs;
+      kvhead = (size_t)hkv * (size_t)a.Nk + ks;
+    } else {
+      Lk = a.Nk;
+      qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+      kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+    }
+  } else {
+    qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+    kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  }
   const unsigned char* Qg = (const unsigned char*)a.q + qhead * ROWB;
   const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
   const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
   const int q0 = iq * BR;
+  if (GEN && q0 >= Lq) return;   // the whole workgroup: past this sequence's queries
   const int qw = q0 + wave * 32;
   const int myq = qw + r32;
   u32x4 qf[NS];
-  if (myq < N) {
+  if (myq < Lq) {
     const unsigned char* qp = Qg + (size_t)myq * ROWB + 16 * hh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = *(const u32x4*)(qp + 32 * s);
@@ -514,10 +535,30 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = u32x4{0, 0, 0, 0};
   }
-  const int nkv = (N + BC - 1) / BC;
-  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
-  const int uhi = qw >= N ? -1 : CAUSAL ? min(qw + 31, N - 1) : N - 1;   // keys some query sees
-  const int whi = CAUSAL ? min(qw, N - 1) : N - 1;                       // keys every query sees
+  // Key tiles t_lo .. t_lo + ntile - 1 (the union of the workgroup's queries' windows);
+  // keys some query of this wave sees: [ulo, uhi] (empty when the wave has no query);
+  // keys every query of it sees: [wlo, whi]; this lane's: [lo_q, hi_q].
+  const int off = Lk - Lq;   // query i sits at key position i + off
+  int t_lo = 0, ntile, ulo = 0, uhi, wlo = 0, whi, lo_q = 0, hi_q = Lk - 1;
+  if constexpr (GEN) {
+    auto lo_of = [&](int i) { return a.wl >= 0 ? i + off - a.wl : 0; };
+    auto hi_of = [&](int i) { return a.wr >= 0 ? min(i + off + a.wr, Lk - 1) : Lk - 1; };
+    const int qlw = min(qw + 31, Lq - 1), qlast = min(q0 + BR, Lq) - 1;
+    lo_q = lo_of(myq);
+    hi_q = hi_of(myq);
+    ulo = max(lo_of(qw), 0);
+    uhi = qw >= Lq ? -1 : hi_of(qlw);
+    wlo = max(lo_of(qlw), 0);
+    whi = hi_of(qw);
+    const int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
+    t_lo = klo / BC;
+    ntile = (Lk <= 0 || khi < klo) ? 0 : khi / BC + 1 - t_lo;
+  } else {
+    const int nkv = (N + BC - 1) / BC;
+    ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+    uhi = qw >= N ? -1 : CAUSAL ? min(qw + 31, N - 1) : N - 1;
+    whi = CAUSAL ? min(qw, N - 1) : N - 1;
+  }
   // K rows (A operand of S^T) and V read transposed (A operand of O^T), as in fwd_kernel
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
@@ -540,7 +581,7 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   // unit u = keys 32u .. 32u+31, half h of the tile in slot sl
   auto unit = [&](int u, const unsigned char* sl, int h) __attribute__((always_inline)) {
     const int k0 = u * 32;
-    if (k0 > uhi) return;   // wave-uniform: no query of this wave sees these keys
+    if (k0 > uhi || k0 + 31 < ulo) return;   // wave-uniform: no query of this wave sees these keys
     f32x16 s;
     u32x4 kf = kread(sl, h, 0);
 #pragma unroll
@@ -550,13 +591,14 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
       s = E::mma(kc, qf[st], st == 0 ? zero16() : s);
     }
     u32x4 vf = vread(sl, h, 0, 0);   // first PV operand, read while the scores settle
-    if (!(k0 + 31 <= whi)) {   // keys past N or (causal) after the query: -inf
-      int lim = N - k0 - 4 * hh;
-      if (CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+    if (!(k0 >= wlo && k0 + 31 <= whi)) {   // keys outside this lane's window or past the end: -inf
+      int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;
+      if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
+      const int llo = lo_q - k0 - 4 * hh;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int oo = 8 * (v >> 2) + (v & 3);
-        if (oo >= lim) s[v] = -INFINITY;
+        if (oo >= lim || (GEN && oo < llo)) s[v] = -INFINITY;
       }
     }
     float mx = s[0];
@@ -593,8 +635,8 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
       o[e] = E::mma(vc, pf[t], o[e]);
     }
   };
-  auto dma = [&](int t, unsigned char* sl) __attribute__((always_inline)) {
-    Tiles::load(Kg, Vg, N, t, wave, doff, sl);
+  auto dma = [&](int j, unsigned char* sl) __attribute__((always_inline)) {
+    Tiles::load(Kg, Vg, Lk, t_lo + j, wave, doff, sl);
   };
   // tile j in slot j % 3: sync, load tile j+2, its two units
   auto tile = [&](auto Tc, int j) __attribute__((always_inline)) {
@@ -605,27 +647,30 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
       __syncthreads();   // everyone's; slot (j-1)%3 is free
     }
     if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
-    unit(2 * j, sc, 0);
-    unit(2 * j + 1, sc, 1);
+    unit(2 * (t_lo + j), sc, 0);
+    unit(2 * (t_lo + j) + 1, sc, 1);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  dma(0, slot0);
-  if (ntile > 1) dma(1, slot1);
-  wait_loads();
-  __syncthreads();
-  for (int j = 0; j < ntile; j += 3) {
-    tile(I0{}, j);
-    if (j + 1 >= ntile) break;
-    tile(I1{}, j + 1);
-    if (j + 2 >= ntile) break;
-    tile(I2{}, j + 2);
+  if (!GEN || ntile > 0) {   // (a mask-family workgroup may have no tile to visit)
+    dma(0, slot0);
+    if (ntile > 1) dma(1, slot1);
+    wait_loads();
+    __syncthreads();
+    for (int j = 0; j < ntile; j += 3) {
+      tile(I0{}, j);
+      if (j + 1 >= ntile) break;
+      tile(I1{}, j + 1);
+      if (j + 2 >= ntile) break;
+      tile(I2{}, j + 2);
+    }
   }
-  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l)
+  // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l); a row that saw no key (mask
+  // family only) gets O = 0 and LSE = -inf
   const float l_tot = half_sum(l_run);
-  if (myq < N) {
-    const float inv = 1.f / l_tot;
+  if (myq < Lq) {
+    const float inv = (GEN && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
     unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -636,7 +681,7 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
                          E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
         *(u32x2*)(Og + d0 * 2) = w;
       }
-    if (hh == 0) a.lse[qhead + myq] = (mr + log2f(l_tot)) * kLn2;
+    if (hh == 0) a.lse[qhead + myq] = (GEN && !(l_tot > 0.f)) ? -INFINITY : (mr + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -653,6 +698,16 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 template <class Tag, int D>
 static hipError_t launch_fwd_masked_t(const FwdArgs& a, hipStream_t stream) {
+  if (a.bidx == nullptr) {   // no block lists: the unit kernel in its general mode
+    constexpr int NW = D == 128 ? 12 : 16;
+    constexpr int BRU = 32 * NW;
+    const long long nb = (long long)a.B * a.Hq * ((a.maxq + BRU - 1) / BRU);
+    if (nb <= 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, false, NW, true>), dim3((unsigned)nb), dim3(NW * 64), 0, stream,
+                       a);
+    return hipGetLastError();
+  }
+  // block lists name 256-query blocks: the 8-wave kernel
   constexpr int BR = 256;
   const int nqb = (a.maxq + BR - 1) / BR;
   const long long nblocks = (long long)a.B * a.Hq * nqb;
