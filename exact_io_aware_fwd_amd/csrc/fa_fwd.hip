@@ -13,9 +13,11 @@
 // realised here inside each wave's instruction stream.
 //
 // gfx950 design.  Two kernels share tiles, layouts and arithmetic:
-//  * fwd_unit_kernel (fa_fwd): 12 waves x 32 query rows at d = 128 (three waves per
-//    SIMD), 16 at d = 64 (four); each wave takes one 32-key unit at a time and the
-//    other waves on its SIMD overlap its softmax with their products.
+//  * fwd_unit_kernel (fa_fwd): NW waves x 32 query rows, each wave taking one 32-key
+//    unit at a time while the other waves on its SIMD overlap its softmax with their
+//    products: at d = 128 12 waves (one workgroup per CU, three waves per SIMD), or 6
+//    (two workgroups per CU) when the 384-row grid would leave CUs idle; at d = 64 8
+//    waves, two workgroups per CU (four waves per SIMD).
 //  * fwd_kernel (the mask family, fa_fwd_masked): 8 waves x 32 rows (256-row blocks,
 //    the granularity of the block lists), two waves per SIMD, with a software
 //    pipeline per wave: the products S_{u+1} = K_{u+1} Q^T are issued while the
@@ -28,8 +30,9 @@
 //    key order inside each 16-key MFMA step is permuted consistently on both
 //    operands, which the sum over keys does not see.
 //  * Q stays in VGPRs for the whole key loop.  K and V tiles of 64 keys go from
-//    HBM straight into LDS (buffer loads to LDS, 16 bytes per lane, three slots
-//    that are distinct LDS objects indexed at compile time, two tiles in flight).
+//    HBM straight into LDS (buffer loads to LDS, 16 bytes per lane, into slots that
+//    are distinct LDS objects indexed at compile time: three slots and two tiles in
+//    flight, or two slots and one where two workgroups share a CU).
 //    Rows are padded to a pitch of row+16 bytes for K and
 //    row+64 bytes for V: with the 64 four-byte banks of the CDNA4 LDS, 16 lanes
 //    reading 16 bytes from 16 consecutive K rows, and 32 lanes reading 8 bytes
@@ -459,19 +462,23 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   }
 }
 
-// The forward without the mask family: NW waves of 32 queries, each taking one 32-key
+// The forward without block lists: NW waves of 32 queries, each taking one 32-key
 // unit at a time — scores, mask, reference max, exponentials and row sum, then
 // O^T += V^T P^T — with no software pipeline: the other waves on the SIMD overlap one
 // wave's softmax with their products.  Without the pipeline's second unit a wave needs
-// ~150 registers at d = 128 (three waves per SIMD: NW = 12) and ~90 at d = 64 (four:
-// NW = 16); two waves per SIMD with the same code run slower than the pipelined kernel
-// above, three and four faster.  Same tiles, loads, layouts, rescaling threshold and
-// epilogue as fwd_kernel, and the same arithmetic in the same order; a unit that no
-// query of a wave sees (past its diagonal, outside its window) is skipped by that
-// wave, which changes no bit.  GEN: the mask family without block lists (lengths,
-// packed batches, windows) as in fwd_kernel.
+// ~150 registers at d = 128 (three waves per SIMD) and ~90 at d = 64 (four); two
+// waves per SIMD with the same code run slower than the pipelined kernel above, three
+// and four faster.  Below 12 waves (6 at d = 128, 8 at d = 64) two LDS slots (75 KB at
+// d = 128, 43 KB at d = 64) leave room for a second workgroup per CU; at 12 three
+// slots keep two tiles in flight.  Same
+// tiles, loads, layouts, rescaling threshold and epilogue as fwd_kernel, and the same
+// arithmetic in the same order, at every NW; a unit that no query of a wave sees
+// (past its diagonal, outside its window) is skipped by that wave, which changes no
+// bit.  GEN: the mask family without block lists (lengths, packed batches, windows)
+// as in fwd_kernel.
 template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
-__global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4)))
+fwd_unit_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
   constexpr int BR = 32 * NW;
   constexpr int BC = 64;
@@ -485,10 +492,12 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   constexpr int NE = D / 32;
   constexpr int NS = D / 16;
   constexpr float TAU = 8.f;
-  // three LDS slots as distinct objects, as in fwd_kernel
+  // NSL LDS slots as distinct objects (see fwd_kernel): three with one workgroup per
+  // CU, two where a second workgroup has to fit beside it
+  constexpr int NSL = NW >= 12 ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[NSL == 3 ? SLOT : 1];
   auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
     return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
   };
@@ -638,15 +647,16 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   auto dma = [&](int j, unsigned char* sl) __attribute__((always_inline)) {
     Tiles::load(Kg, Vg, Lk, t_lo + j, wave, doff, sl);
   };
-  // tile j in slot j % 3: sync, load tile j+2, its two units
+  // tile j in slot j % NSL: sync, load tile j + NSL - 1 into the slot tile j-1 used,
+  // its two units
   auto tile = [&](auto Tc, int j) __attribute__((always_inline)) {
     constexpr int T = decltype(Tc)::value;
     unsigned char* const sc = slot(T);
     if (j > 0) {
       wait_loads();      // this wave's loads of tile j landed
-      __syncthreads();   // everyone's; slot (j-1)%3 is free
+      __syncthreads();   // everyone's; everyone is done with tile j-1
     }
-    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    if (j + NSL - 1 < ntile) dma(j + NSL - 1, slot((T + NSL - 1) % NSL));
     unit(2 * (t_lo + j), sc, 0);
     unit(2 * (t_lo + j) + 1, sc, 1);
   };
@@ -655,15 +665,17 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
   using I2 = std::integral_constant<int, 2>;
   if (!GEN || ntile > 0) {   // (a mask-family workgroup may have no tile to visit)
     dma(0, slot0);
-    if (ntile > 1) dma(1, slot1);
+    if (NSL == 3 && ntile > 1) dma(1, slot1);
     wait_loads();
     __syncthreads();
-    for (int j = 0; j < ntile; j += 3) {
+    for (int j = 0; j < ntile; j += NSL) {
       tile(I0{}, j);
       if (j + 1 >= ntile) break;
       tile(I1{}, j + 1);
-      if (j + 2 >= ntile) break;
-      tile(I2{}, j + 2);
+      if constexpr (NSL == 3) {
+        if (j + 2 >= ntile) break;
+        tile(I2{}, j + 2);
+      }
     }
   }
   // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l); a row that saw no key (mask
@@ -686,27 +698,44 @@ __global__ void __launch_bounds__(NW * 64) fwd_unit_kernel(const FwdArgs a) {
 }
 
 
+// Waves per workgroup of fwd_unit_kernel.  d = 64: 8 (two workgroups per CU beat one
+// of 16 at every measured shape).  d = 128: 12, one workgroup of 384 rows per CU; 6
+// (192 rows, two per CU) when the 384-row grid is small — at most 128 workgroups, or
+// 256 when causal, where a single long diagonal block would otherwise set the time.
+// Past that the 6-wave grid loses: two workgroups per CU load every K/V tile twice.
+template <int D>
+static int fwd_unit_waves(long long rows_blocks_of_384, bool causal) {
+  if (D != 128) return 8;
+  return rows_blocks_of_384 <= (causal ? 256 : 128) ? 6 : 12;
+}
+
+template <class Tag, int D, bool CAUSAL, bool GEN>
+static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStream_t stream) {
+  const long long bh = (long long)a.B * a.Hq;
+  const int nw = fwd_unit_waves<D>(bh * ((nq + 383) / 384), causal);
+  const int br = 32 * nw;
+  const long long nb = bh * ((nq + br - 1) / br);
+  if (nb <= 0) return hipSuccess;
+  if constexpr (D == 128) {
+    if (nw == 6)
+      hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, 6, GEN>), dim3((unsigned)nb), dim3(6 * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, 12, GEN>), dim3((unsigned)nb), dim3(12 * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, 8, GEN>), dim3((unsigned)nb), dim3(8 * 64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = D == 128 ? 12 : 16;
-  constexpr int BR = 32 * NW;
-  const long long nb = (long long)a.B * a.Hq * ((a.N + BR - 1) / BR);
-  if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, NW>), dim3((unsigned)nb), dim3(NW * 64), 0, stream, a);
-  return hipGetLastError();
+  return launch_fwd_unit<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
 }
 
 template <class Tag, int D>
 static hipError_t launch_fwd_masked_t(const FwdArgs& a, hipStream_t stream) {
-  if (a.bidx == nullptr) {   // no block lists: the unit kernel in its general mode
-    constexpr int NW = D == 128 ? 12 : 16;
-    constexpr int BRU = 32 * NW;
-    const long long nb = (long long)a.B * a.Hq * ((a.maxq + BRU - 1) / BRU);
-    if (nb <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, false, NW, true>), dim3((unsigned)nb), dim3(NW * 64), 0, stream,
-                       a);
-    return hipGetLastError();
-  }
+  if (a.bidx == nullptr)   // no block lists: the unit kernel in its general mode
+    return launch_fwd_unit<Tag, D, false, true>(a, a.maxq, a.wr >= 0, stream);
   // block lists name 256-query blocks: the 8-wave kernel
   constexpr int BR = 256;
   const int nqb = (a.maxq + BR - 1) / BR;

@@ -109,6 +109,27 @@ def test_gqa_head_mapping():
             assert torch.all(o[b, h] == float(b * Hkv + h // (Hq // Hkv))), (b, h)
 
 
+@pytest.mark.parametrize("causal,hq", [(False, 128), (True, 256)])
+def test_workgroup_shape_does_not_change_bits(causal, hq):
+    """At d = 128 the forward runs 6-wave (192-row) workgroups when the 384-row grid is
+    small (at most 128 blocks, 256 when causal) and 12-wave ones otherwise.  One more
+    query head crosses that line: the heads both calls share must come out bit for bit
+    the same, and the oracle checks the first and the extra head of the larger call."""
+    N, d = 300, 128
+    q, k, v = workloads.random_case(31 + hq, 1, hq + 1, 1, N, d, torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    say(f"[fwd] workgroup shape: Hq={hq} vs {hq + 1} (MQA) N={N} causal={causal}")
+    qd, kd, vd = to_dev(q, k, v)
+    o_small, l_small = fa.fwd(qd[:, :hq].contiguous(), kd, vd, causal=causal, softmax_scale=scale)
+    o_big, l_big = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_small, o_big[:, :hq]) and torch.equal(l_small, l_big[:, :hq])
+    for h in (0, hq):
+        O_ref, L_ref = oracle.attention_fwd(q[:, h:h + 1], k, v, causal, scale)
+        assert o_err(o_big[:, h:h + 1].cpu(), O_ref) <= O_TOL[torch.bfloat16]
+        assert np.abs(l_big[:, h:h + 1].cpu().double().numpy() - L_ref).max() <= LSE_TOL
+
+
 def test_forward_is_bitwise_deterministic():
     w = workloads.WORKLOADS["b4_h32_n4096_d128_bf16_causal_qx8"]
     q, k, v = to_dev(*workloads.random_case(9, 2, 8, 2, 2048, 128, torch.bfloat16))
