@@ -15,7 +15,8 @@
 // once more, needs no atomics and no fp32 dQ buffer, and is bitwise reproducible.
 //
 //  1. row terms: LSE_i * log2(e) and D_i = sum_k dO_ik O_ik in fp32, as pairs;
-//  2. dQ pass: one workgroup of 8 waves per (batch, head, 256-query block), the
+//  2. dQ pass: one workgroup of 8 waves per (batch, head, 256-query block) — 4 waves
+//     and 128 queries, two workgroups per CU, at d = 64 and for small grids — the
 //     forward's structure: S^T = K Q^T and dP^T = V dO^T with Q, dO in VGPRs and K
 //     (XOR-swizzled: read by rows and transposed), V tiles streamed through LDS;
 //     P = exp2(S*scale*log2e - LSE*log2e),
@@ -776,7 +777,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
 // PIPE: the next unit's products interleaved with this unit's elementwise work (two
 // units of S, dP live at once); otherwise one unit at a time.
 template <class Tag, int D, bool CAUSAL, int NW, bool PIPE, bool GEN = false>
-__global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) bwd_dq_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
   constexpr int BR = 32 * NW;           // query rows per workgroup
@@ -792,11 +793,14 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   constexpr int NE = D / 32;            // 32-row blocks of dQ^T
   constexpr int NS = D / 16;            // k-steps of S^T and dP^T
 
-  // Three slots as distinct LDS objects (see the dK/dV pass): tile j uses slot j % 3,
-  // known at compile time in the 3-tile unrolled loops.
+  // NSL slots as distinct LDS objects (see the dK/dV pass): tile j uses slot j % NSL,
+  // known at compile time in the NSL-tile unrolled loops.  Three (two tiles in flight)
+  // unless two 4-wave workgroups must share a CU at d = 128 (33 KB a slot).
+  constexpr int NSL = (D == 128 && NW < 8) ? 2 : 3;
+  static_assert(!PIPE || NSL == 3, "the pipeline reads the next tile before its barrier");
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[NSL == 3 ? SLOT : 1];
   auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
     return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
   };
@@ -901,8 +905,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
     }
     P1 = min(max(P1, 0), ntile);
     P2 = min(max(P2, 0), ntile);
-    JH = min(ntile, (P1 + 2) / 3 * 3);
-    JT = max(JH, P2 / 3 * 3);
+    JH = min(ntile, (P1 + NSL - 1) / NSL * NSL);
+    JT = max(JH, P2 / NSL * NSL);
   } else {
     ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
     whi = CAUSAL ? min(qw, N - 1) : N - 1;
@@ -1066,18 +1070,18 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   };
 
   f32x16 sa, pa, sb, pb;
-  // Tile j (slot T = j % 3): sync, load tile j+2, units 2j (S, dP in sa, pa) and 2j+1
-  // (in sb, pb).  With PIPE, the products of the unit after the last are formed from a
-  // valid slot and never used.
+  // Tile j (slot T = j % NSL): sync, load tile j + NSL - 1 into the slot tile j-1 used,
+  // units 2j (S, dP in sa, pa) and 2j+1 (in sb, pb).  With PIPE, the products of the
+  // unit after the last are formed from a valid slot and never used.
   auto tile = [&](auto Tc, auto MASK, int j) __attribute__((always_inline)) {
     constexpr int T = decltype(Tc)::value;
     unsigned char* const sc = slot(T);
-    unsigned char* const sn = slot((T + 1) % 3);
+    unsigned char* const sn = slot((T + 1) % NSL);
     if (j > 0) {
-      wait_loads();      // this wave's loads of tile j+1 landed
-      __syncthreads();   // everyone's; slot (j-1)%3 is free
+      wait_loads();      // this wave's loads of tiles up to j + 1 (NSL = 3), j (NSL = 2)
+      __syncthreads();   // everyone's; everyone is done with tile j-1
     }
-    if (j + 2 < ntile) dma(j + 2, slot((T + 2) % 3));
+    if (j + NSL - 1 < ntile) dma(j + NSL - 1, slot((T + NSL - 1) % NSL));
     if constexpr (PIPE) {
       step(MASK, 2 * j, sc, 0, sc, 1, sa, pa, sb, pb);
       step(MASK, 2 * j + 1, sc, 1, sn, 0, sb, pb, sa, pa);
@@ -1094,7 +1098,7 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
 
   if (!GEN || ntile > 0) {   // (a mask-family workgroup may have no key tile)
   dma(0, slot0);
-  if (ntile > 1) dma(1, slot1);
+  if (NSL == 3 && ntile > 1) dma(1, slot1);
   wait_loads();
   __syncthreads();
   if constexpr (PIPE) {
@@ -1109,28 +1113,32 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   // Tiles whose units all precede every wave's last unit need no mask.
   if constexpr (!GEN) {
     const int ulast0 = (CAUSAL ? min(q0 + 31, N - 1) : N - 1) / 32;
-    JT = min(ntile, ulast0 / 2) / 3 * 3;
+    JT = min(ntile, ulast0 / 2) / NSL * NSL;
   }
   int j = 0;
-  for (; j < JH; j += 3) {
+  for (; j < JH; j += NSL) {
     tile(I0{}, Masked{}, j);
     if (j + 1 >= ntile) break;
     tile(I1{}, Masked{}, j + 1);
-    if (j + 2 >= ntile) break;
-    tile(I2{}, Masked{}, j + 2);
+    if constexpr (NSL == 3) {
+      if (j + 2 >= ntile) break;
+      tile(I2{}, Masked{}, j + 2);
+    }
   }
   j = JH;
-  for (; j < JT; j += 3) {
+  for (; j < JT; j += NSL) {
     tile(I0{}, Plain{}, j);
     tile(I1{}, Plain{}, j + 1);
-    tile(I2{}, Plain{}, j + 2);
+    if constexpr (NSL == 3) tile(I2{}, Plain{}, j + 2);
   }
-  for (; j < ntile; j += 3) {
+  for (; j < ntile; j += NSL) {
     tile(I0{}, Masked{}, j);
     if (j + 1 >= ntile) break;
     tile(I1{}, Masked{}, j + 1);
-    if (j + 2 >= ntile) break;
-    tile(I2{}, Masked{}, j + 2);
+    if constexpr (NSL == 3) {
+      if (j + 2 >= ntile) break;
+      tile(I2{}, Masked{}, j + 2);
+    }
   }
   }
   acc_drain(acc);
@@ -1151,6 +1159,31 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a) {
   }
 }
 
+// Waves per workgroup of the dQ pass (two waves per SIMD either way): 8 (256 queries,
+// one workgroup per CU) or 4 (two per CU).  d = 64: 4 (51 KB of LDS each; measured as
+// fast or faster at every shape).  d = 128: 4 only while the 256-row grid is small —
+// at most 128 workgroups, or 256 when causal — where it would leave CUs idle; past
+// that the two workgroups' separate K/V streams cost 1-3 %.
+template <int D>
+static int dq_waves(long long blocks_of_256, bool causal) {
+  if (D != 128) return 4;
+  return blocks_of_256 <= (causal ? 256 : 128) ? 4 : 8;
+}
+
+template <class Tag, int D, bool CAUSAL, bool GEN>
+static hipError_t launch_dq(const BwdArgs& a, int nq, bool causal, hipStream_t stream) {
+  const long long bh = (long long)a.B * a.Hq;
+  constexpr bool PIPE = D != 128;   // d = 128: one unit at a time (see the dQ pass)
+  if (dq_waves<D>(bh * ((nq + 255) / 256), causal) == 4) {
+    const long long nb = bh * ((nq + 127) / 128);
+    hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, 4, PIPE, GEN>), dim3((unsigned)nb), dim3(4 * 64), 0, stream, a);
+  } else {
+    const long long nb = bh * ((nq + 255) / 256);
+    hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, 8, PIPE, GEN>), dim3((unsigned)nb), dim3(8 * 64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const long long prows = (long long)a.B * a.Hq * ((a.N + 31) / 32) * 32;   // padded rows
@@ -1160,12 +1193,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, a, prows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // 8 waves (2 per SIMD); at d = 128 one unit at a time (see the dQ pass)
-  constexpr int NWQ = 8;
-  const long long nqb = (a.N + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, NWQ, D != 128>), dim3((unsigned)(nqb * a.B * a.Hq)),
-                     dim3(NWQ * 64), 0, stream, a);
-  err = hipGetLastError();
+  err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
   if (err != hipSuccess) return err;
   const long long nkb = (a.N + 127) / 128;
   hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
@@ -1182,11 +1210,7 @@ static hipError_t launch_bwd_masked_t(const BwdArgs& a, hipStream_t stream) {
                      stream, a, prows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  constexpr int NWQ = 8;
-  const long long nqb = (a.maxq + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, false, NWQ, D != 128, true>), dim3((unsigned)(nqb * a.B * a.Hq)), dim3(NWQ * 64),
-                     0, stream, a);
-  err = hipGetLastError();
+  err = launch_dq<Tag, D, false, true>(a, a.maxq, a.wr >= 0, stream);
   if (err != hipSuccess) return err;
   const long long nkb = (a.maxk + 127) / 128;
   if (nkb <= 0) return hipSuccess;

@@ -91,6 +91,30 @@ def test_constant_v_gives_zero_dq_dk():
     assert rel_l2(dv.cpu(), dV) <= GRAD_TOL
 
 
+@pytest.mark.parametrize("causal,hq", [(False, 64), (True, 128)])
+def test_dq_workgroup_shape_does_not_change_bits(causal, hq):
+    """At d = 128 the dQ pass runs 4-wave (128-query) workgroups when the 256-row grid is
+    small (at most 128 blocks, 256 when causal) and 8-wave ones otherwise.  One more
+    query head (N = 300: two blocks a head) crosses that line: dQ of the heads both calls
+    share must agree bit for bit, and the oracle checks dQ of the first and the extra head
+    of the larger call (dK, dV sum over all heads of the group, so they differ)."""
+    N, d = 300, 128
+    q, k, v = workloads.random_case(41 + hq, 1, hq + 1, 1, N, d, torch.bfloat16)
+    do = workloads.randn(43 + hq, (1, hq + 1, N, d), torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    say(f"[bwd] dQ workgroup shape: Hq={hq} vs {hq + 1} (MQA) N={N} causal={causal}")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+    sub = [t[:, :hq].contiguous() for t in (qd, o, lse, dod)]
+    dq_small = fa.bwd(sub[0], kd, vd, sub[1], sub[2], sub[3], causal=causal, softmax_scale=scale)[0]
+    dq_big = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, softmax_scale=scale)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(dq_small, dq_big[:, :hq])
+    for h in (0, hq):
+        dQ = oracle.attention_bwd(q[:, h:h + 1], k, v, do[:, h:h + 1], causal, scale)[0]
+        assert rel_l2(dq_big[:, h:h + 1].cpu(), dQ) <= GRAD_TOL
+
+
 def test_backward_is_bitwise_deterministic():
     q, k, v, do = (t.to("cuda:0") for t in workloads.random_case(21, 2, 8, 2, 1500, 128, torch.bfloat16, with_do=True))
     o, lse = fa.fwd(q, k, v, causal=True)
