@@ -274,10 +274,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype,
                              int causal) {
-  (void)causal;
   bool empty = false;
   if (check_sizes(B, Hq, Hkv, N, d, dtype, &empty) != FA_OK) return 0;
-  return fa::bwd_rowterm_bytes(B, Hq, N);
+  return fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -296,7 +295,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
       (st = check_ptr(dq, "dq")) != FA_OK || (st = check_ptr(dk, "dk")) != FA_OK ||
       (st = check_ptr(dv, "dv")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
     return st;
-  const size_t need = fa::bwd_rowterm_bytes(B, Hq, N);
+  const size_t need = fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -318,6 +317,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.N = (int)N;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * kLog2e;
+  a.ksplit = fa::bwd_dense_split(B, Hq, Hkv, N, causal != 0);
+  if (a.ksplit > 1) a.pool = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::bwd_pool_offset(B, Hq, N));
   const hipError_t err = fa::launch_bwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
   return FA_OK;

@@ -307,7 +307,7 @@ __device__ __forceinline__ void dkdv_dma(const unsigned char* qh, const unsigned
   }
 }
 
-template <class Tag, int D, bool CAUSAL, bool GEN = false>
+template <class Tag, int D, bool CAUSAL, bool GEN = false, bool SPLIT = false>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
@@ -349,6 +349,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   // primary block of a split key block has nothing to do.
   const int ngroups = a.B * a.Hkv;
   const int nkbg = GEN ? (a.maxk + BKV - 1) / BKV : 0;
+  const int nsplit = SPLIT ? a.ksplit : 1;   // fa_bwd: chunks per key block
   int bid = blockIdx.x;
   int jb, grp, chunk = 0;
   bool mapped = false;
@@ -363,14 +364,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     }
     bid -= kBwdSlots;   // a multiple of 8: the XCD of each primary block is unchanged
   }
-  if (!mapped) {
+  if (!mapped) {   // (the nsplit chunks of a key block follow each other, heaviest blocks first)
     if ((ngroups & 7) == 0) {
       const int x = bid & 7, sidx = bid >> 3, per = ngroups >> 3;
-      jb = sidx / per;
-      grp = x + 8 * (sidx - jb * per);
+      jb = sidx / (per * nsplit);
+      const int rest = sidx - jb * per * nsplit;
+      if constexpr (SPLIT) chunk = rest / per;
+      grp = x + 8 * (rest - chunk * per);
     } else {
-      jb = bid / ngroups;
-      grp = bid - jb * ngroups;
+      jb = bid / (ngroups * nsplit);
+      const int rest = bid - jb * ngroups * nsplit;
+      if constexpr (SPLIT) chunk = rest / ngroups;
+      grp = rest - chunk * ngroups;
     }
     if (GEN && a.plan != nullptr && a.plan[2 * (grp * nkbg + jb)] > 1) return;
   }
@@ -423,6 +428,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const int* runs = nullptr;
   int nruns = 0, run0 = 0, skip0 = 0;   // with lists: the chunk starts skip0 steps into run run0
   int nchunk = 1, pslot = 0;            // chunks of this key block, this chunk's partial slot
+  int s0 = 0;                           // fa_bwd split: this chunk's first step
   if constexpr (GEN) {
     static_assert(BKV == 128 && BQ == 32, "dkdv_query_range and the runs assume these");
     const bool any = dkdv_query_range(a, Lq, Lk, k0, qlo, qtop);
@@ -453,6 +459,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     qtop = (nb32 - 1) * BQ;
     qlo = CAUSAL ? k0 : 0;
     nsteps = G * ((qtop - qlo) / BQ + 1);
+    if (SPLIT) {   // this chunk's steps [s0, s0 + nsteps) of the key block's sequence
+      const int total = nsteps, per = (total + nsplit - 1) / nsplit;
+      s0 = min(chunk * per, total);
+      nsteps = min(s0 + per, total) - s0;
+      nchunk = nsplit;
+      pslot = (grp * ((N + BKV - 1) / BKV) + jb) * nsplit + chunk;
+    }
   }
 
   // ---- HBM -> LDS (step n into slot n % 3), driven by a cursor over (head, block) ----
@@ -471,6 +484,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   const float* dr_h = r_g;
   const int hbytes = Lq * ROWB, rbytes = nb32 * 256;   // buffer ranges: rows past Lq read 0
   int dqb = qtop;   // query block of the next step to load
+  if (SPLIT && s0 > 0) {   // a later chunk: start s0 steps in (heads outer, blocks descending)
+    const int spb = (qtop - qlo) / BQ + 1, g0 = s0 / spb;
+    dqb = qtop - BQ * (s0 - g0 * spb);
+    dq_h += (size_t)g0 * hs * ROWB;
+    dg_h += (size_t)g0 * hs * ROWB;
+    dr_h += (long long)g0 * nb32 * 64;
+  }
   // block lists: run dri of the records, steps left in it, its tiles
   int dri = 0, dleft = 0, dtiles = 3;
   auto load_run = [&](int r) __attribute__((always_inline)) {
@@ -551,7 +571,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   //   dK^T += Q^T dS.
   // dP_{n+1} starts from -D, so dP - D comes out of the MFMA.  The products of a step
   // past the last are formed anyway from a valid slot and never used.
-  int cqb_plain = qtop;   // query block of the current step (GEN: recorded per slot)
+  int cqb_plain = dqb;    // query block of the current step (GEN: recorded per slot)
   f32x16 l2n;             // LSE*log2e of the current step's rows
   auto step = [&](auto Jc, int n, f32x16& sc, f32x16& dpc, f32x16& sn, f32x16& dpn) __attribute__((always_inline)) {
     constexpr int J = decltype(Jc)::value;
@@ -698,7 +718,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   acc_drain(dk);
   acc_drain(dv);
 
-  if (GEN && nchunk > 1) {
+  if ((GEN || SPLIT) && nchunk > 1) {
     // one chunk of a split key block: fp32 partial dK^T (unscaled), dV^T as [key][d]
     float* pk = a.pool + (size_t)pslot * 2 * BKV * D + (size_t)(32 * wave + r32) * D;
     float* pv = pk + BKV * D;
@@ -736,22 +756,38 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 // One workgroup per slot: the slot of chunk c of a key block split n ways takes keys
 // [128c/n, 128(c+1)/n) of the block, sums the n partials (consecutive slots) in chunk
 // order and writes dK = scale * sum, dV = sum in the input dtype.
+// Without a slot table (fa_bwd's split): key block `rec` owns slots rec*ksplit ..
+// rec*ksplit + ksplit - 1.
 template <class Tag, int D>
 __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   constexpr int ROWB = D * 2;
-  if ((int)blockIdx.x >= a.table[0]) return;
-  const int c = a.table[2 + 2 * blockIdx.x];
-  const int sl = blockIdx.x - c;   // chunk 0's slot
-  const int rec = a.table[1 + 2 * blockIdx.x];
-  const int nkbg = (a.maxk + 127) / 128;
-  const int grp = rec / nkbg, jb = rec - grp * nkbg;
-  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
-  int Lq, Lk, qs, ks;
-  seq_geometry(a, b, Lq, Lk, qs, ks);
-  const size_t kvhead =
-      a.cu_q != nullptr ? (size_t)hkv * (size_t)a.Nk + ks : (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
-  const int n = a.plan[2 * rec];
+  int c, sl, rec, n, jb, Lk;   // chunk, chunk 0's slot, record, chunks, key block, keys
+  size_t kvhead;
+  if (a.table != nullptr) {
+    if ((int)blockIdx.x >= a.table[0]) return;
+    c = a.table[2 + 2 * blockIdx.x];
+    sl = blockIdx.x - c;
+    rec = a.table[1 + 2 * blockIdx.x];
+    const int nkbg = (a.maxk + 127) / 128;
+    const int grp = rec / nkbg;
+    jb = rec - grp * nkbg;
+    const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
+    int Lq, qs, ks;
+    seq_geometry(a, b, Lq, Lk, qs, ks);
+    kvhead = a.cu_q != nullptr ? (size_t)hkv * (size_t)a.Nk + ks : (size_t)(b * a.Hkv + hkv) * (size_t)a.Nk;
+    n = a.plan[2 * rec];
+  } else {
+    n = a.ksplit;
+    rec = blockIdx.x / n;
+    c = blockIdx.x - rec * n;
+    sl = rec * n;
+    const int nkb = (a.N + 127) / 128;
+    const int grp = rec / nkb;
+    jb = rec - grp * nkb;
+    Lk = a.N;
+    kvhead = (size_t)grp * (size_t)a.N;   // grp = batch * Hkv + K/V head
+  }
   const int k0 = jb * 128;
   const int key0 = 128 * c / n, nk = 128 * (c + 1) / n - key0;
   for (int i = threadIdx.x; i < 2 * nk * (D / 8); i += 256) {
@@ -1195,9 +1231,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
   if (err != hipSuccess) return err;
-  const long long nkb = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)(nkb * a.B * a.Hkv)), dim3(256), 0,
+  const long long nrec = (a.N + 127) / 128 * a.B * a.Hkv;
+  if (a.ksplit == 1) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL, false, true>), dim3((unsigned)(nrec * a.ksplit)), dim3(256), 0,
                      stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_reduce_kernel<Tag, D>), dim3((unsigned)(nrec * a.ksplit)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

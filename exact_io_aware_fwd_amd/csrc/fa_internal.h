@@ -60,6 +60,10 @@ struct BwdArgs {
   int* plan = nullptr;
   int* table = nullptr;
   float* pool = nullptr;
+  // fa_bwd with few key blocks for the CUs: the query steps of every key block are split
+  // into ksplit chunks, whose partial dK, dV go to `pool` (ksplit consecutive slots per
+  // key block, record = (batch * Hkv + K/V head) * key blocks + key block)
+  int ksplit = 1;
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
@@ -151,6 +155,32 @@ hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, f
 // multiple of 32 per head (256 bytes per 32-row block).
 inline size_t bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)(B * Hq * ((N + 31) / 32) * 256);
+}
+// fa_bwd: with fewer 128-key blocks than the CUs can take at once — 256, or 512 when
+// causal, where the blocks' step counts range over the whole sequence — each key block's
+// query steps are split into k chunks (at most 16; the longest block's chunks at least
+// kBwdSplitMinSteps steps, below which writing and summing the partials cost more than
+// the balance gains) whose fp32 partial dK, dV are summed in chunk order afterwards; 1
+// means no split.
+constexpr int kBwdSplitMinSteps = 32;
+inline int bwd_dense_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal) {
+  const int64_t R = B * Hkv * ((N + 127) / 128);
+  if (R <= 0 || Hkv <= 0) return 1;
+  int64_t k = (causal ? 512 : 256) / R;
+  const int64_t steps = (Hq / Hkv) * ((N + 31) / 32);   // the longest key block's steps
+  k = k < 16 ? k : 16;
+  k = k < steps / kBwdSplitMinSteps ? k : steps / kBwdSplitMinSteps;
+  return (int)(k > 1 ? k : 1);
+}
+// fa_bwd workspace: the row terms, then (split) the partial slots, 2 x 128 keys x d fp32
+// each, from a 256-byte boundary.
+inline size_t bwd_pool_offset(int64_t B, int64_t Hq, int64_t N) {
+  return (bwd_rowterm_bytes(B, Hq, N) + 255) / 256 * 256;
+}
+inline size_t bwd_dense_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, bool causal) {
+  const int k = bwd_dense_split(B, Hq, Hkv, N, causal);
+  if (k == 1) return bwd_rowterm_bytes(B, Hq, N);
+  return bwd_pool_offset(B, Hq, N) + (size_t)(B * Hkv * ((N + 127) / 128)) * k * 2 * 128 * (size_t)d * 4;
 }
 // Block lists in the masked backward.  The dK/dV pass splits a key block whose
 // transposed list names more query steps than its share (total steps / kBwdTargetChunks,

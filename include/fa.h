@@ -73,8 +73,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: two fp32 terms per query
  * row, LSE_i * log2(e) and -D_i with D_i = sum_k dO_ik O_ik, rows padded to a multiple
- * of 32 per head, i.e. 8 * B * Hq * 32 * ceil(N / 32) bytes.  Returns 0 for invalid
- * sizes.
+ * of 32 per head, i.e. R = 8 * B * Hq * 32 * ceil(N / 32) bytes.  When the sizes give
+ * fewer 128-key blocks (B * Hkv * ceil(N / 128)) than 256 (512 when causal), the dK/dV
+ * pass splits each block's query steps into k chunks (k <= 16, at least 32 steps of
+ * 32 queries in the longest block's chunks) and the workspace also holds their
+ * fp32 partial dK, dV: R rounded up to 256, plus blocks * k * 2 * 128 * d * 4 bytes
+ * (at most 512 slots, 64 MiB at d = 128).  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                              fa_dtype dtype, int causal);

@@ -100,11 +100,27 @@ def test_bwd_workspace_too_small(L):
     assert "workspace" in binding.last_error()
 
 
+def _dense_split(B, Hq, Hkv, N, causal):
+    """Chunks per 128-key block of fa_bwd's dK/dV pass: enough to give the CUs 256 (512
+    when causal) workgroups, at most 16, each at least 32 query steps of the longest block."""
+    R = B * Hkv * -(-N // 128)
+    k = min((512 if causal else 256) // R, 16, (Hq // Hkv) * -(-N // 32) // 32)
+    return max(k, 1)
+
+
 def test_workspace_size_values(L):
-    # two fp32 row terms (LSE*log2e, -D) per query row, rows padded to 32 per head
-    for B, Hq, Hkv, N, d in ((1, 16, 16, 4096, 128), (2, 32, 8, 8192, 128), (1, 1, 1, 1, 64), (3, 6, 2, 1000, 64)):
-        got = L.fa_bwd_workspace_size(B, Hq, Hkv, N, d, 1, 1)
-        assert got == B * Hq * ((N + 31) // 32) * 32 * 8
+    # two fp32 row terms (LSE*log2e, -D) per query row, rows padded to 32 per head; with few
+    # key blocks, then the partial dK/dV slots of the split key blocks from a 256-byte boundary
+    for B, Hq, Hkv, N, d in ((1, 16, 16, 4096, 128), (2, 32, 8, 8192, 128), (1, 1, 1, 1, 64), (3, 6, 2, 1000, 64),
+                             (1, 8, 1, 1000, 128), (1, 32, 8, 1024, 64), (1, 4, 4, 70000, 128)):
+        for causal in (0, 1):
+            got = L.fa_bwd_workspace_size(B, Hq, Hkv, N, d, 1, causal)
+            rt = B * Hq * ((N + 31) // 32) * 32 * 8
+            k = _dense_split(B, Hq, Hkv, N, causal)
+            want = rt if k == 1 else -(-rt // 256) * 256 + B * Hkv * -(-N // 128) * k * 2 * 128 * d * 4
+            assert got == want, (B, Hq, Hkv, N, d, causal, got, want)
+    assert _dense_split(2, 32, 8, 8192, 1) == 1 and _dense_split(1, 8, 1, 1000, 1) == 8
+    assert _dense_split(1, 16, 16, 4096, 1) == 1 and _dense_split(1, 32, 8, 4096, 1) == 2
     assert L.fa_bwd_workspace_size(1, 3, 2, 16, 64, 1, 0) == 0
     assert L.fa_bwd_workspace_size(1, 2, 1, 16, 96, 1, 0) == 0
 

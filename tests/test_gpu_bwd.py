@@ -59,6 +59,9 @@ def test_small_and_ragged(N, d, dtype):
     (1, 8, 1, 600, 128, torch.bfloat16),
     (1, 6, 2, 777, 128, torch.float16),
     (2, 4, 4, 513, 128, torch.bfloat16),
+    # few key blocks: the dK/dV pass splits each block's query steps (11, 16 chunks)
+    (1, 16, 1, 700, 64, torch.float16),
+    (1, 32, 2, 1100, 128, torch.bfloat16),
 ], ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}")
 def test_multi_tile_tails(case):
     B, Hq, Hkv, N, d, dt = case
