@@ -15,6 +15,7 @@ of the same workload on the host cores.
     python bench.py --decode [--steps K] ...    # split-KV decoding: GB/s against the HBM peak
     python bench.py --fp8 [--steps K] ...       # FP8 forward (quantise + attention): TFLOP/s
     python bench.py --masks [--steps K] ...     # mask-family forward (sliding window; varlen, block-sparse)
+    python bench.py --sweep                     # fa_fwd / fa_bwd TFLOP/s over 128 shapes (markdown table)
 
 Profiling helpers (rocprofv3 runs of this same script):
     python bench.py --copy-calibration          # a plain 1 GiB device copy, for HBM counters
@@ -64,6 +65,8 @@ def parse():
                    help="with --masks: skip the workloads timed alongside (profiling runs)")
     p.add_argument("--fp8", action="store_true",
                    help="time the FP8 forward (block quantisation with the Hadamard transform + attention)")
+    p.add_argument("--sweep", action="store_true",
+                   help="fa_fwd and fa_bwd TFLOP/s over a grid of shapes (bf16; markdown table) and exit")
     return p.parse_args()
 
 
@@ -479,6 +482,62 @@ def bench_masks(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_sweep(args):
+    """Forward and backward TFLOP/s (algorithmic FLOPs / time with HIP events on the launch
+    stream, best of three rounds of 10 calls each) over d in {128, 64}, (B, Hq, Hkv) in
+    {(1, 16, 16), (1, 32, 8), (2, 32, 8), (4, 32, 8)}, N from 1K to 16K (at most 1M query
+    rows), causal or not; seeded N(0, 1) bf16 inputs."""
+    import torch
+    import workloads
+    import exact_io_aware_fwd_amd as fa
+    from exact_io_aware_fwd_amd import metrics
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def best_ms(fn, reps=10, rounds=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps)
+        return best
+
+    warm_until = time.perf_counter() + 0.3    # let the clocks ramp before the first shape
+    print("| d | B | Hq/Hkv | N | causal | fa_fwd ms | fwd TFLOP/s | fa_bwd ms | bwd TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|", flush=True)
+    for d in (128, 64):
+        for (B, Hq, Hkv) in ((1, 16, 16), (1, 32, 8), (2, 32, 8), (4, 32, 8)):
+            for N in (1024, 2048, 4096, 8192, 16384):
+                if B * Hq * N > 2 * 32 * 16384:
+                    continue
+                q, k, v, do = (workloads.randn(1000 + i, (B, h, N, d), torch.bfloat16).to(dev)
+                               for i, h in enumerate((Hq, Hkv, Hkv, Hq)))
+                for causal in (True, False):
+                    o = torch.empty_like(q)
+                    lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+                    ws = torch.empty(max(fa.bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype, causal), 16),
+                                     dtype=torch.uint8, device=dev)
+                    fwd = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+                    while time.perf_counter() < warm_until:
+                        fwd()
+                        torch.cuda.synchronize()
+                    tf = best_ms(fwd)
+                    tb = best_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws))
+                    ff = metrics.fwd_flops(B, Hq, N, d, causal)
+                    fb = metrics.bwd_flops(B, Hq, N, d, causal)
+                    print(f"| {d} | {B} | {Hq}/{Hkv} | {N} | {'yes' if causal else 'no'} | {tf:.4f} | "
+                          f"{ff / tf / 1e9:.0f} | {tb:.4f} | {fb / tb / 1e9:.0f} |", flush=True)
+                del q, k, v, do
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -502,6 +561,9 @@ def main():
         return
     if args.decode:
         bench_decode(args)
+        return
+    if args.sweep:
+        bench_sweep(args)
         return
 
     import torch
