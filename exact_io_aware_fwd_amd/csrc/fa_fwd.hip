@@ -626,12 +626,11 @@ fwd_unit_kernel(const FwdArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
     }
-    float rs = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s[v] = fast_exp2(fmaf(s[v], c2, -mref));
-      rs += s[v];
-    }
+    for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], c2, -mref));
+    float rs = s[0];   // (not 0 + s[0]: P is never -0, so the same value, one add less)
+#pragma unroll
+    for (int v = 1; v < 16; ++v) rs += s[v];
     l_run = fmaf(l_run, alpha, rs);
     const u32x4 pf[2] = {
         u32x4{E::pack(s[0], s[1]), E::pack(s[2], s[3]), E::pack(s[4], s[5]), E::pack(s[6], s[7])},
