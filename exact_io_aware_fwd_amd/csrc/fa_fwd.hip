@@ -617,15 +617,19 @@ fwd_unit_kernel(const FwdArgs a) {
     // the reference max moves only when a row's max passes it by TAU (log2 units)
     const bool raise = mx > mr + TAU;
     const float mnew = raise ? mx : mr;
-    const float alpha = (mr == -INFINITY) ? 0.f : fast_exp2(mr - mnew);
     const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    mr = mnew;
+    // alpha = 2^(m_old - m_new) is exactly 1 on every lane when no lane of the wave moved
+    // its reference (a lane whose reference is still -inf has l = 0, where alpha does not
+    // matter), so it is formed only when some lane did
+    float alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      alpha = (mr == -INFINITY) ? 0.f : fast_exp2(mr - mnew);
 #pragma unroll
       for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
     }
+    mr = mnew;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], c2, -mref));
     float rs = s[0];   // (not 0 + s[0]: P is never -0, so the same value, one add less)
