@@ -1197,12 +1197,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 
 // Waves per workgroup of the dQ pass (two waves per SIMD either way): 8 (256 queries,
 // one workgroup per CU) or 4 (two per CU).  d = 64: 4 (51 KB of LDS each; measured as
-// fast or faster at every shape).  d = 128: 4 only while the 256-row grid is small —
-// at most 128 workgroups, or 256 when causal — where it would leave CUs idle; past
-// that the two workgroups' separate K/V streams cost 1-3 %.
+// fast or faster at every shape).  d = 128: 4 while the 256-row grid is small — at most
+// 128 workgroups, or 256 when causal — where it would leave CUs idle, and under a
+// window whose left side is shorter than 2048 keys, where a workgroup's key span
+// (window + its rows) exceeds each wave's (window + 32) by a large fraction and the
+// narrower workgroup wastes less; elsewhere the two workgroups' separate K/V streams
+// cost 1-3 %.
 template <int D>
-static int dq_waves(long long blocks_of_256, bool causal) {
+static int dq_waves(long long blocks_of_256, bool causal, int window_left) {
   if (D != 128) return 4;
+  if (window_left >= 0 && window_left < 2048) return 4;
   return blocks_of_256 <= (causal ? 256 : 128) ? 4 : 8;
 }
 
@@ -1210,7 +1214,7 @@ template <class Tag, int D, bool CAUSAL, bool GEN>
 static hipError_t launch_dq(const BwdArgs& a, int nq, bool causal, hipStream_t stream) {
   const long long bh = (long long)a.B * a.Hq;
   constexpr bool PIPE = D != 128;   // d = 128: one unit at a time (see the dQ pass)
-  if (dq_waves<D>(bh * ((nq + 255) / 256), causal) == 4) {
+  if (dq_waves<D>(bh * ((nq + 255) / 256), causal, GEN ? a.wl : -1) == 4) {
     const long long nb = bh * ((nq + 127) / 128);
     hipLaunchKernelGGL((bwd_dq_kernel<Tag, D, CAUSAL, 4, PIPE, GEN>), dim3((unsigned)nb), dim3(4 * 64), 0, stream, a);
   } else {
