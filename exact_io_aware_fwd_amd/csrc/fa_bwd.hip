@@ -33,7 +33,9 @@
 //     HBM -> LDS directly (three slots, two steps in flight).  Per step:
 //     S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P, dK^T += Q^T dS (Q^T,
 //     dO^T read transposed from LDS); the products of step n+1 are interleaved
-//     with the elementwise work of step n.
+//     with the elementwise work of step n.  Where 256-key blocks still give the CUs
+//     enough workgroups (512, or 256 without the causal mask), fa_bwd runs instead
+//     4 waves x 64 keys (3b below): half the LDS reads per product.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -752,6 +754,280 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   }
 }
 
+// ---- 3b. dK, dV with 64 keys per wave (fa_bwd where the 256-key grid fills the CUs) -----
+// Four waves x 64 keys: each wave holds K and V of two 32-key halves and their dK^T, dV^T
+// (all 256 accumulator registers), so every Q / dO operand read from LDS feeds two
+// products, half the LDS bytes per product of the 32-key pass, whose one wave per SIMD
+// cannot pull more LDS bandwidth than it uses.  No room is left for a software pipeline;
+// instead each step orders its work so that the vector ALU runs under the matrix cores:
+// the S products; the dP products, each slot with a share of P's exponentials; the dV
+// products (they need only P), each slot with a share of dS = P * (dP - D); the dK
+// products.  Per key, the same operations in the same order as the 32-key pass (steps a
+// wave cannot see add nothing), so both give the same bits.
+template <class Tag, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
+  using E = Elt<Tag>;
+  using A = AccMma<Tag>;
+  constexpr int NW = 4;
+  constexpr int KW = 64;
+  constexpr int BKV = KW * NW;
+  constexpr int BQ = 32;
+  constexpr int ROWB = D * 2;
+  constexpr int CH = D / 8;
+  constexpr int NS = D / 16;
+  constexpr int NE = D / 32;
+  constexpr int TB = BQ * ROWB;
+  constexpr int TI = TB / 1024;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int LI = 2 * TI / NW;
+  constexpr int RT = 2 * TB;
+  constexpr int SLOT = 2 * TB + 256;
+  static_assert(TI % NW == 0, "each wave loads whole Q / dO halves");
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5, r32 = lane & 31;
+  const int N = a.N;
+  const int G = a.Hq / a.Hkv;
+  const int ngroups = a.B * a.Hkv;
+  const int bid = blockIdx.x;
+  int jb, grp;
+  if ((ngroups & 7) == 0) {
+    const int x = bid & 7, sidx = bid >> 3, per = ngroups >> 3;
+    jb = sidx / per;
+    grp = x + 8 * (sidx - jb * per);
+  } else {
+    jb = bid / ngroups;
+    grp = bid - jb * ngroups;
+  }
+  const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  const size_t qrow0 = (size_t)(b * a.Hq + hkv * G) * (size_t)N;
+  const size_t hs = (size_t)N;
+  const int k0 = jb * BKV;
+  const int kw = k0 + KW * wave;
+  u32x4 kf[2][NS], vf[2][NS];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int key = kw + 32 * h + r32;
+    if (key < N) {
+      const unsigned char* kp = (const unsigned char*)a.k + (kvhead + key) * ROWB + 16 * hh;
+      const unsigned char* vp = (const unsigned char*)a.v + (kvhead + key) * ROWB + 16 * hh;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        kf[h][st] = *(const u32x4*)(kp + 32 * st);
+        vf[h][st] = *(const u32x4*)(vp + 32 * st);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) kf[h][st] = vf[h][st] = u32x4{0, 0, 0, 0};
+    }
+  }
+  const int nb32 = (N + 31) / 32;
+  const int qtop = (nb32 - 1) * BQ;
+  const int qlo = CAUSAL ? k0 : 0;
+  const int nsteps = G * ((qtop - qlo) / BQ + 1);
+  int soff[LI];
+#pragma unroll
+  for (int i = 0; i < LI; ++i) {
+    const int nn = wave + NW * i;
+    const int row = (nn % TI) * RPI + lane / CH;
+    soff[i] = row * ROWB + (((lane % CH) ^ swz<CH>(row)) << 4);
+  }
+  const unsigned char* dq_h = (const unsigned char*)a.q + qrow0 * ROWB;
+  const unsigned char* dg_h = (const unsigned char*)a.dout + qrow0 * ROWB;
+  const float* dr_h = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
+  const int hbytes = N * ROWB, rbytes = nb32 * 256;
+  int dqb = qtop;
+  int sqb[3];
+  auto dma_next = [&](unsigned char* sl, int si) __attribute__((always_inline)) {
+    dkdv_dma<ROWB, TI, LI, NW, TB>(dq_h, dg_h, dr_h, hbytes, rbytes, dqb * ROWB, dqb * 8, wave, lane, soff, sl);
+    sqb[si] = dqb;
+    dqb -= BQ;
+    if (dqb < qlo) {
+      dqb = qtop;
+      dq_h += hs * ROWB;
+      dg_h += hs * ROWB;
+      dr_h += nb32 * 64;
+    }
+  };
+  using SO = SwzOffsets<ROWB>;
+  const int ra0 = SO::rows_a0(lane);
+  const int trl = SO::tr_lane(lane);
+  auto rowrd = [&](const unsigned char* sl, int st) __attribute__((always_inline)) {
+    return *(const u32x4*)(sl + (ra0 ^ (st << 5)));
+  };
+  auto trrd = [&](const unsigned char* sl, int t, int e) __attribute__((always_inline)) {
+    return cat(lds_read_tr(sl + 16 * t * ROWB + (trl ^ SO::tr_inst(e, 0))),
+               lds_read_tr(sl + (16 * t + 8) * ROWB + (trl ^ SO::tr_inst(e, 1))));
+  };
+  auto rt16 = [&](const unsigned char* sl, int off) __attribute__((always_inline)) {
+    f32x16 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 t = *(const f32x4*)(sl + RT + off + (8 * j + 4 * hh) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[4 * j + i] = t[i];
+    }
+    return r;
+  };
+  auto pack = [&](const f32x16& x, int t) __attribute__((always_inline)) {
+    return u32x4{E::pack(x[8 * t + 0], x[8 * t + 1]), E::pack(x[8 * t + 2], x[8 * t + 3]),
+                 E::pack(x[8 * t + 4], x[8 * t + 5]), E::pack(x[8 * t + 6], x[8 * t + 7])};
+  };
+  f32x16 dk0[NE], dk1[NE], dv0[NE], dv1[NE];
+  acc_init(dk0);
+  acc_init(dk1);
+  acc_init(dv0);
+  acc_init(dv1);
+  const float c2 = a.scale_log2;
+  // S products; then the dP products, each slot with four of P's exponentials; then the dV
+  // products (they need only P), each slot with four of dS's products; then the dK products
+  auto step = [&](auto Sc) __attribute__((always_inline)) {
+    constexpr int SI = decltype(Sc)::value;
+    unsigned char* const bc = slot(SI);
+    const int cqb = sqb[SI];
+    if (CAUSAL && cqb + BQ - 1 < kw) return;   // every query of the step before every key of the wave
+    f32x16 s0, s1, p0, p1;
+    {
+      u32x4 qa = rowrd(bc, 0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 qc = qa;
+        if (st + 1 < NS) qa = rowrd(bc, st + 1);
+        s0 = E::mma(qc, kf[0][st], st == 0 ? zero16() : s0);
+        s1 = E::mma(qc, kf[1][st], st == 0 ? zero16() : s1);
+      }
+    }
+    const bool diag = CAUSAL && cqb < kw + KW - 1;
+    {
+      const f32x16 l2 = rt16(bc, 0);
+      const f32x16 nd = rt16(bc, 128);
+      u32x4 ga = rowrd(bc + TB, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 gc = ga;
+        if (st + 1 < NS) ga = rowrd(bc + TB, st + 1);
+#pragma unroll
+        for (int v = (16 * st) / NS; v < (16 * (st + 1)) / NS; ++v) {
+          s0[v] = fast_exp2(fmaf(s0[v], c2, -l2[v]));
+          s1[v] = fast_exp2(fmaf(s1[v], c2, -l2[v]));
+          keep(s0[v]);
+          keep(s1[v]);
+        }
+        p0 = E::mma(gc, vf[0][st], st == 0 ? nd : p0);
+        p1 = E::mma(gc, vf[1][st], st == 0 ? nd : p1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (diag) {   // query cqb + 8(v/4) + 4hh + v%4 before the key: P = 0
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int qi = cqb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (kw + r32 > qi) s0[v] = 0.f;
+        if (kw + 32 + r32 > qi) s1[v] = 0.f;
+      }
+    }
+    const u32x4 pf0[2] = {pack(s0, 0), pack(s0, 1)};
+    const u32x4 pf1[2] = {pack(s1, 0), pack(s1, 1)};
+    keep(pf0[0]);
+    keep(pf0[1]);
+    keep(pf1[0]);
+    keep(pf1[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      u32x4 ta = trrd(bc + TB, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NE; ++k) {
+        const u32x4 tc = ta;
+        if (k + 1 < 2 * NE) ta = trrd(bc + TB, (k + 1) / NE, (k + 1) % NE);
+#pragma unroll
+        for (int v = (16 * k) / (2 * NE); v < (16 * (k + 1)) / (2 * NE); ++v) {
+          p0[v] = s0[v] * p0[v];
+          p1[v] = s1[v] * p1[v];
+          keep(p0[v]);
+          keep(p1[v]);
+        }
+        if (k == 0) A::mma_fresh(dv0[k % NE], tc, pf0[k / NE]);
+        else A::mma(dv0[k % NE], tc, pf0[k / NE]);
+        A::mma(dv1[k % NE], tc, pf1[k / NE]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const u32x4 sf0[2] = {pack(p0, 0), pack(p0, 1)};
+    const u32x4 sf1[2] = {pack(p1, 0), pack(p1, 1)};
+    keep(sf0[0]);
+    keep(sf0[1]);
+    keep(sf1[0]);
+    keep(sf1[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      u32x4 tb = trrd(bc, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NE; ++k) {
+        const u32x4 td = tb;
+        if (k + 1 < 2 * NE) tb = trrd(bc, (k + 1) / NE, (k + 1) % NE);
+        if (k == 0) A::mma_fresh(dk0[k % NE], td, sf0[k / NE]);
+        else A::mma(dk0[k % NE], td, sf0[k / NE]);
+        A::mma(dk1[k % NE], td, sf1[k / NE]);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  auto iter = [&](auto Jc, int n) __attribute__((always_inline)) {
+    constexpr int J = decltype(Jc)::value;
+    if (n > 0) {
+      wait_loads();
+      __syncthreads();
+    }
+    if (n + 2 < nsteps) dma_next(slot((J + 2) % 3), (J + 2) % 3);
+    step(Jc);
+  };
+  if (nsteps > 0) {
+    dma_next(slot0, 0);
+    if (nsteps > 1) dma_next(slot1, 1);
+    wait_loads();
+    __syncthreads();
+    for (int n = 0; n < nsteps; n += 3) {
+      iter(I0{}, n);
+      if (n + 1 >= nsteps) break;
+      iter(I1{}, n + 1);
+      if (n + 2 >= nsteps) break;
+      iter(I2{}, n + 2);
+    }
+  }
+  acc_drain(dk0);
+  acc_drain(dk1);
+  acc_drain(dv0);
+  acc_drain(dv1);
+  auto store = [&](const f32x16 (&dk)[NE], const f32x16 (&dv)[NE], int key) __attribute__((always_inline)) {
+    if (key >= N) return;
+    unsigned char* dKg = (unsigned char*)a.dk + (kvhead + key) * ROWB;
+    unsigned char* dVg = (unsigned char*)a.dv + (kvhead + key) * ROWB;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * e + 8 * g4 + 4 * hh;
+        const u32x2 wk = {E::pack(dk[e][4 * g4 + 0] * a.scale, dk[e][4 * g4 + 1] * a.scale),
+                          E::pack(dk[e][4 * g4 + 2] * a.scale, dk[e][4 * g4 + 3] * a.scale)};
+        const u32x2 wv = {E::pack(dv[e][4 * g4 + 0], dv[e][4 * g4 + 1]), E::pack(dv[e][4 * g4 + 2], dv[e][4 * g4 + 3])};
+        *(u32x2*)(dKg + d0 * 2) = wk;
+        *(u32x2*)(dVg + d0 * 2) = wv;
+      }
+  };
+  store(dk0, dv0, kw + r32);
+  store(dk1, dv1, kw + 32 + r32);
+}
+
 // ---- sum of the partial dK, dV of split key blocks ----------------------------------------
 // One workgroup per slot: the slot of chunk c of a key block split n ways takes keys
 // [128c/n, 128(c+1)/n) of the block, sums the n partials (consecutive slots) in chunk
@@ -1236,6 +1512,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
   if (err != hipSuccess) return err;
   const long long nrec = (a.N + 127) / 128 * a.B * a.Hkv;
+  const long long nrec256 = (a.N + 255) / 256 * a.B * a.Hkv;
+  if (nrec256 >= (CAUSAL ? 512 : 256)) {   // 64 keys a wave (then a.ksplit == 1)
+    hipLaunchKernelGGL((bwd_dkdv64_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec256), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.ksplit == 1) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec), dim3(256), 0, stream, a);
     return hipGetLastError();
