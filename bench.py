@@ -482,6 +482,16 @@ def bench_masks(args):
     print(json.dumps(rec), flush=True)
 
 
+def _dkdv_kernels(B, Hq, Hkv, N, causal):
+    """The dK/dV launches fa_bwd makes for these sizes (its choice, restated for the label):
+    64 keys a wave where 256-key blocks number at least 512 (256 without the causal mask),
+    else 32 keys a wave, its key blocks split into chunks (and a reduction) when few."""
+    if -(-N // 256) * B * Hkv >= (512 if causal else 256):
+        return "bwd_dkdv64_kernel", 3
+    k = min((512 if causal else 256) // (-(-N // 128) * B * Hkv), 16, (Hq // Hkv) * -(-N // 32) // 32)
+    return ("bwd_dkdv_kernel + bwd_reduce_kernel", 4) if k > 1 else ("bwd_dkdv_kernel", 3)
+
+
 def bench_sweep(args):
     """Forward and backward TFLOP/s (algorithmic FLOPs / time with HIP events on the launch
     stream, best of three rounds of 10 calls each) over d in {128, 64}, (B, Hq, Hkv) in
@@ -619,7 +629,8 @@ def main():
                       "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12}}
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
     if not args.fwd_only:
-        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "launches": 3,
+        dkdv, nl = _dkdv_kernels(w.B, w.Hq, w.Hkv, w.N, causal)
+        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_dq_kernel + " + dkdv, "launches": nl,
                          "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12}
         passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
     def roofline(kind):
