@@ -118,6 +118,27 @@ def test_dq_workgroup_shape_does_not_change_bits(causal, hq):
         assert rel_l2(dq_big[:, h:h + 1].cpu(), dQ) <= GRAD_TOL
 
 
+@pytest.mark.parametrize("d,dt", [(64, torch.float16), (128, torch.float16), (64, torch.bfloat16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dkdv_64_key_waves_sampled_heads(d, dt, causal):
+    """4 x 16 heads of 2100 tokens give 576 blocks of 256 keys, so the dK/dV pass runs 64
+    keys a wave (ragged tail included).  Every head is its own K/V group: the oracle checks
+    the first and the last (batch, head) whole."""
+    B, H, N = 4, 16, 2100
+    q, k, v, do = (workloads.randn(60 + i, (B, H, N, d), dt) for i in range(4))
+    scale = 1 / math.sqrt(d)
+    say(f"[bwd] 64-key dK/dV waves: B={B} H={H} N={N} d={d} {dt} causal={causal}")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], causal, scale)
+        for x, r in zip((dq, dk, dv), ref):
+            assert rel_l2(x[sl].cpu(), r) <= GRAD_TOL, (b, h)
+
+
 def test_backward_is_bitwise_deterministic():
     q, k, v, do = (t.to("cuda:0") for t in workloads.random_case(21, 2, 8, 2, 1500, 128, torch.bfloat16, with_do=True))
     o, lse = fa.fwd(q, k, v, causal=True)
