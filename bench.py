@@ -484,12 +484,14 @@ def bench_masks(args):
 
 def _dkdv_kernels(B, Hq, Hkv, N, causal):
     """The dK/dV launches fa_bwd makes for these sizes (its choice, restated for the label):
-    64 keys a wave where 256-key blocks number at least 512 (256 without the causal mask),
-    else 32 keys a wave, its key blocks split into chunks (and a reduction) when few."""
-    if -(-N // 256) * B * Hkv >= (512 if causal else 256):
-        return "bwd_dkdv64_kernel", 3
-    k = min((512 if causal else 256) // (-(-N // 128) * B * Hkv), 16, (Hq // Hkv) * -(-N // 32) // 32)
-    return ("bwd_dkdv_kernel + bwd_reduce_kernel", 4) if k > 1 else ("bwd_dkdv_kernel", 3)
+    records of 256 keys (64 a wave) or 128, split into chunks (and a reduction) when few."""
+    steps, target = (Hq // Hkv) * -(-N // 32), 512 if causal else 256
+    chunks = lambda r, m: max(min(target // r, 16, steps // m), 1)
+    r256, r128 = B * Hkv * -(-N // 256), B * Hkv * -(-N // 128)
+    name, k = (("bwd_dkdv64_kernel", chunks(r256, 256))
+               if r256 >= target or r256 * chunks(r256, 256) >= r128 * chunks(r128, 32)
+               else ("bwd_dkdv_kernel", chunks(r128, 32)))
+    return (name + " + bwd_reduce_kernel", 4) if k > 1 else (name, 3)
 
 
 def bench_sweep(args):

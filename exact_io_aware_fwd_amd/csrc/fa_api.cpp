@@ -317,7 +317,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.N = (int)N;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * kLog2e;
-  a.ksplit = fa::bwd_dense_split(B, Hq, Hkv, N, causal != 0);
+  const fa::BwdDensePlan plan = fa::bwd_dense_plan(B, Hq, Hkv, N, causal != 0);
+  a.kblock = plan.kblock;
+  a.ksplit = plan.ksplit;
   if (a.ksplit > 1) a.pool = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::bwd_pool_offset(B, Hq, N));
   const hipError_t err = fa::launch_bwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));

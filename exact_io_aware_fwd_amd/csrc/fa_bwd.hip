@@ -764,7 +764,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
 // products (they need only P), each slot with a share of dS = P * (dP - D); the dK
 // products.  Per key, the same operations in the same order as the 32-key pass (steps a
 // wave cannot see add nothing), so both give the same bits.
-template <class Tag, int D, bool CAUSAL>
+template <class Tag, int D, bool CAUSAL, bool SPLIT = false>
 __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   using A = AccMma<Tag>;
@@ -794,16 +794,22 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
   const int G = a.Hq / a.Hkv;
+  // block -> (key block, chunk, batch, K/V head) as in the 32-key pass
   const int ngroups = a.B * a.Hkv;
+  const int nsplit = SPLIT ? a.ksplit : 1;
   const int bid = blockIdx.x;
-  int jb, grp;
+  int jb, grp, chunk = 0;
   if ((ngroups & 7) == 0) {
     const int x = bid & 7, sidx = bid >> 3, per = ngroups >> 3;
-    jb = sidx / per;
-    grp = x + 8 * (sidx - jb * per);
+    jb = sidx / (per * nsplit);
+    const int rest = sidx - jb * per * nsplit;
+    if constexpr (SPLIT) chunk = rest / per;
+    grp = x + 8 * (rest - chunk * per);
   } else {
-    jb = bid / ngroups;
-    grp = bid - jb * ngroups;
+    jb = bid / (ngroups * nsplit);
+    const int rest = bid - jb * ngroups * nsplit;
+    if constexpr (SPLIT) chunk = rest / ngroups;
+    grp = rest - chunk * ngroups;
   }
   const int b = grp / a.Hkv, hkv = grp - b * a.Hkv;
   const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
@@ -831,7 +837,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
   const int nb32 = (N + 31) / 32;
   const int qtop = (nb32 - 1) * BQ;
   const int qlo = CAUSAL ? k0 : 0;
-  const int nsteps = G * ((qtop - qlo) / BQ + 1);
+  int nsteps = G * ((qtop - qlo) / BQ + 1);
+  int s0 = 0;
+  if constexpr (SPLIT) {   // this chunk's steps [s0, s0 + nsteps)
+    const int total = nsteps, per = (total + nsplit - 1) / nsplit;
+    s0 = min(chunk * per, total);
+    nsteps = min(s0 + per, total) - s0;
+  }
   int soff[LI];
 #pragma unroll
   for (int i = 0; i < LI; ++i) {
@@ -844,6 +856,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
   const float* dr_h = a.rowterm + (long long)(b * a.Hq + hkv * G) * nb32 * 64;
   const int hbytes = N * ROWB, rbytes = nb32 * 256;
   int dqb = qtop;
+  if (SPLIT && s0 > 0) {   // a later chunk: start s0 steps in (heads outer, blocks descending)
+    const int spb = (qtop - qlo) / BQ + 1, g0 = s0 / spb;
+    dqb = qtop - BQ * (s0 - g0 * spb);
+    dq_h += (size_t)g0 * hs * ROWB;
+    dg_h += (size_t)g0 * hs * ROWB;
+    dr_h += (long long)g0 * nb32 * 64;
+  }
   int sqb[3];
   auto dma_next = [&](unsigned char* sl, int si) __attribute__((always_inline)) {
     dkdv_dma<ROWB, TI, LI, NW, TB>(dq_h, dg_h, dr_h, hbytes, rbytes, dqb * ROWB, dqb * 8, wave, lane, soff, sl);
@@ -1024,6 +1043,27 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
         *(u32x2*)(dVg + d0 * 2) = wv;
       }
   };
+  if constexpr (SPLIT) {
+    if (nsplit > 1) {   // fp32 partial dK^T (unscaled) then dV^T of the 256 keys, as [key][d]
+      const int pslot = (grp * ((N + BKV - 1) / BKV) + jb) * nsplit + chunk;
+      float* pk = a.pool + (size_t)pslot * 2 * BKV * D;
+      auto part = [&](const f32x16 (&acc)[NE], float* base, int lkey) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = 32 * e + 8 * g4 + 4 * hh;
+            *(f32x4*)(base + (size_t)lkey * D + d0) =
+                f32x4{acc[e][4 * g4], acc[e][4 * g4 + 1], acc[e][4 * g4 + 2], acc[e][4 * g4 + 3]};
+          }
+      };
+      part(dk0, pk, KW * wave + r32);
+      part(dk1, pk, KW * wave + 32 + r32);
+      part(dv0, pk + BKV * D, KW * wave + r32);
+      part(dv1, pk + BKV * D, KW * wave + 32 + r32);
+      return;
+    }
+  }
   store(dk0, dv0, kw + r32);
   store(dk1, dv1, kw + 32 + r32);
 }
@@ -1032,13 +1072,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
 // One workgroup per slot: the slot of chunk c of a key block split n ways takes keys
 // [128c/n, 128(c+1)/n) of the block, sums the n partials (consecutive slots) in chunk
 // order and writes dK = scale * sum, dV = sum in the input dtype.
-// Without a slot table (fa_bwd's split): key block `rec` owns slots rec*ksplit ..
-// rec*ksplit + ksplit - 1.
+// Without a slot table (fa_bwd's split): record `rec` (a.kblock keys) owns slots
+// rec*ksplit .. rec*ksplit + ksplit - 1.
 template <class Tag, int D>
 __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
   using E = Elt<Tag>;
   constexpr int ROWB = D * 2;
-  int c, sl, rec, n, jb, Lk;   // chunk, chunk 0's slot, record, chunks, key block, keys
+  int c, sl, rec, n, jb, Lk, kb = 128;   // chunk, chunk 0's slot, record, chunks, key block, keys, keys a record
   size_t kvhead;
   if (a.table != nullptr) {
     if ((int)blockIdx.x >= a.table[0]) return;
@@ -1055,17 +1095,18 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
     n = a.plan[2 * rec];
   } else {
     n = a.ksplit;
+    kb = a.kblock;
     rec = blockIdx.x / n;
     c = blockIdx.x - rec * n;
     sl = rec * n;
-    const int nkb = (a.N + 127) / 128;
+    const int nkb = (a.N + kb - 1) / kb;
     const int grp = rec / nkb;
     jb = rec - grp * nkb;
     Lk = a.N;
     kvhead = (size_t)grp * (size_t)a.N;   // grp = batch * Hkv + K/V head
   }
-  const int k0 = jb * 128;
-  const int key0 = 128 * c / n, nk = 128 * (c + 1) / n - key0;
+  const int k0 = jb * kb;
+  const int key0 = kb * c / n, nk = kb * (c + 1) / n - key0;
   for (int i = threadIdx.x; i < 2 * nk * (D / 8); i += 256) {
     const int t = i / (nk * (D / 8));   // 0: dK, 1: dV
     const int e8 = i - t * nk * (D / 8);
@@ -1073,7 +1114,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
     if (k0 + key >= Lk) continue;
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < n; ++c) {
-      const float* p = a.pool + ((size_t)(sl + c) * 2 + t) * 128 * D + (size_t)key * D + d0;
+      const float* p = a.pool + ((size_t)(sl + c) * 2 + t) * kb * D + (size_t)key * D + d0;
       lo += *(const f32x4*)p;
       hi += *(const f32x4*)(p + 4);
     }
@@ -1511,12 +1552,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
   if (err != hipSuccess) return err;
-  const long long nrec = (a.N + 127) / 128 * a.B * a.Hkv;
-  const long long nrec256 = (a.N + 255) / 256 * a.B * a.Hkv;
-  if (nrec256 >= (CAUSAL ? 512 : 256)) {   // 64 keys a wave (then a.ksplit == 1)
-    hipLaunchKernelGGL((bwd_dkdv64_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec256), dim3(256), 0, stream, a);
+  if (a.kblock == 256) {   // 64 keys a wave
+    const long long nrec256 = (a.N + 255) / 256 * a.B * a.Hkv;
+    if (a.ksplit == 1) {
+      hipLaunchKernelGGL((bwd_dkdv64_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec256), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((bwd_dkdv64_kernel<Tag, D, CAUSAL, true>), dim3((unsigned)(nrec256 * a.ksplit)), dim3(256), 0,
+                       stream, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_reduce_kernel<Tag, D>), dim3((unsigned)(nrec256 * a.ksplit)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
+  const long long nrec = (a.N + 127) / 128 * a.B * a.Hkv;
   if (a.ksplit == 1) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)nrec), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -64,6 +64,7 @@ struct BwdArgs {
   // into ksplit chunks, whose partial dK, dV go to `pool` (ksplit consecutive slots per
   // key block, record = (batch * Hkv + K/V head) * key blocks + key block)
   int ksplit = 1;
+  int kblock = 128;   // fa_bwd: keys per dK/dV record, 256 (64 keys a wave) or 128 (32)
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
@@ -156,31 +157,47 @@ hipError_t launch_lse_combine(const float* opart, const float* lpart, void* o, f
 inline size_t bwd_rowterm_bytes(int64_t B, int64_t Hq, int64_t N) {
   return (size_t)(B * Hq * ((N + 31) / 32) * 256);
 }
-// fa_bwd: with fewer 128-key blocks than the CUs can take at once — 256, or 512 when
-// causal, where the blocks' step counts range over the whole sequence — each key block's
-// query steps are split into k chunks (at most 16; the longest block's chunks at least
-// kBwdSplitMinSteps steps, below which writing and summing the partials cost more than
-// the balance gains) whose fp32 partial dK, dV are summed in chunk order afterwards; 1
-// means no split.
+// fa_bwd's dK/dV pass: records of 256 keys (64 keys a wave) or 128 (32 a wave).  A
+// record's query steps may be split into k chunks (at most 16) whose fp32 partial dK, dV
+// are summed in chunk order afterwards, so that the records and their chunks give the
+// CUs 256 workgroups, or 512 when causal (where the records' step counts range over the
+// whole sequence).  The longest record's chunks keep at least kBwdSplitMinSteps steps
+// (256-key records: kBwdSplitMinSteps256, their partials being twice as large), below
+// which writing and summing the partials cost more than the balance gains.  256-key
+// records are used whenever they give as many workgroups as 128-key ones (half the LDS
+// reads per product); 128-key ones remain for the smaller grids.
 constexpr int kBwdSplitMinSteps = 32;
-inline int bwd_dense_split(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal) {
-  const int64_t R = B * Hkv * ((N + 127) / 128);
-  if (R <= 0 || Hkv <= 0) return 1;
-  int64_t k = (causal ? 512 : 256) / R;
-  const int64_t steps = (Hq / Hkv) * ((N + 31) / 32);   // the longest key block's steps
+constexpr int kBwdSplitMinSteps256 = 256;
+struct BwdDensePlan {
+  int kblock;   // keys per record
+  int ksplit;   // chunks per record (1: no split)
+};
+inline int bwd_dense_chunks(int64_t records, int64_t steps, bool causal, int min_steps) {
+  if (records <= 0) return 1;
+  int64_t k = (causal ? 512 : 256) / records;
   k = k < 16 ? k : 16;
-  k = k < steps / kBwdSplitMinSteps ? k : steps / kBwdSplitMinSteps;
+  k = k < steps / min_steps ? k : steps / min_steps;
   return (int)(k > 1 ? k : 1);
 }
-// fa_bwd workspace: the row terms, then (split) the partial slots, 2 x 128 keys x d fp32
-// each, from a 256-byte boundary.
+inline BwdDensePlan bwd_dense_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, bool causal) {
+  if (Hkv <= 0 || N <= 0) return {128, 1};
+  const int64_t steps = (Hq / Hkv) * ((N + 31) / 32);   // the longest record's steps
+  const int64_t r256 = B * Hkv * ((N + 255) / 256), r128 = B * Hkv * ((N + 127) / 128);
+  const int k256 = bwd_dense_chunks(r256, steps, causal, kBwdSplitMinSteps256);
+  const int k128 = bwd_dense_chunks(r128, steps, causal, kBwdSplitMinSteps);
+  if (r256 >= (causal ? 512 : 256) || r256 * k256 >= r128 * k128) return {256, k256};
+  return {128, k128};
+}
+// fa_bwd workspace: the row terms, then (split) the partial slots, 2 x kblock keys x d
+// fp32 each, from a 256-byte boundary.
 inline size_t bwd_pool_offset(int64_t B, int64_t Hq, int64_t N) {
   return (bwd_rowterm_bytes(B, Hq, N) + 255) / 256 * 256;
 }
 inline size_t bwd_dense_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, bool causal) {
-  const int k = bwd_dense_split(B, Hq, Hkv, N, causal);
-  if (k == 1) return bwd_rowterm_bytes(B, Hq, N);
-  return bwd_pool_offset(B, Hq, N) + (size_t)(B * Hkv * ((N + 127) / 128)) * k * 2 * 128 * (size_t)d * 4;
+  const BwdDensePlan pl = bwd_dense_plan(B, Hq, Hkv, N, causal);
+  if (pl.ksplit == 1) return bwd_rowterm_bytes(B, Hq, N);
+  const int64_t records = B * Hkv * ((N + pl.kblock - 1) / pl.kblock);
+  return bwd_pool_offset(B, Hq, N) + (size_t)records * pl.ksplit * 2 * pl.kblock * (size_t)d * 4;
 }
 // Block lists in the masked backward.  The dK/dV pass splits a key block whose
 // transposed list names more query steps than its share (total steps / kBwdTargetChunks,

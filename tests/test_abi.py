@@ -100,12 +100,21 @@ def test_bwd_workspace_too_small(L):
     assert "workspace" in binding.last_error()
 
 
-def _dense_split(B, Hq, Hkv, N, causal):
-    """Chunks per 128-key block of fa_bwd's dK/dV pass: enough to give the CUs 256 (512
-    when causal) workgroups, at most 16, each at least 32 query steps of the longest block."""
-    R = B * Hkv * -(-N // 128)
-    k = min((512 if causal else 256) // R, 16, (Hq // Hkv) * -(-N // 32) // 32)
-    return max(k, 1)
+def _dense_plan(B, Hq, Hkv, N, causal):
+    """fa_bwd's dK/dV records (256 or 128 keys) and chunks per record: chunks enough to give
+    the CUs 256 (512 when causal) workgroups, at most 16, each at least 32 query steps of the
+    longest record (256 for 256-key records); 256-key records when they reach that alone or
+    give as many workgroups."""
+    steps = (Hq // Hkv) * -(-N // 32)
+    target = 512 if causal else 256
+
+    def chunks(r, m):
+        return max(min(target // r, 16, steps // m), 1)
+
+    r256, r128 = B * Hkv * -(-N // 256), B * Hkv * -(-N // 128)
+    if r256 >= target or r256 * chunks(r256, 256) >= r128 * chunks(r128, 32):
+        return 256, chunks(r256, 256)
+    return 128, chunks(r128, 32)
 
 
 def test_workspace_size_values(L):
@@ -116,11 +125,12 @@ def test_workspace_size_values(L):
         for causal in (0, 1):
             got = L.fa_bwd_workspace_size(B, Hq, Hkv, N, d, 1, causal)
             rt = B * Hq * ((N + 31) // 32) * 32 * 8
-            k = _dense_split(B, Hq, Hkv, N, causal)
-            want = rt if k == 1 else -(-rt // 256) * 256 + B * Hkv * -(-N // 128) * k * 2 * 128 * d * 4
+            kb, k = _dense_plan(B, Hq, Hkv, N, causal)
+            want = rt if k == 1 else -(-rt // 256) * 256 + B * Hkv * -(-N // kb) * k * 2 * kb * d * 4
             assert got == want, (B, Hq, Hkv, N, d, causal, got, want)
-    assert _dense_split(2, 32, 8, 8192, 1) == 1 and _dense_split(1, 8, 1, 1000, 1) == 8
-    assert _dense_split(1, 16, 16, 4096, 1) == 1 and _dense_split(1, 32, 8, 4096, 1) == 2
+    assert _dense_plan(2, 32, 8, 8192, 1) == (256, 1) and _dense_plan(1, 8, 1, 1000, 1) == (128, 8)
+    assert _dense_plan(1, 16, 16, 4096, 1) == (128, 1) and _dense_plan(1, 32, 8, 8192, 1) == (256, 2)
+    assert _dense_plan(1, 16, 16, 1024, 1) == (128, 1) and _dense_plan(1, 16, 16, 2048, 1) == (128, 2)
     assert L.fa_bwd_workspace_size(1, 3, 2, 16, 64, 1, 0) == 0
     assert L.fa_bwd_workspace_size(1, 2, 1, 16, 96, 1, 0) == 0
 
