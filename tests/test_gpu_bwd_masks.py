@@ -247,6 +247,39 @@ def test_bwd_masked_equals_bwd_bitwise(B, causal):
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d,dt,window", [(128, torch.bfloat16, (200, 0)), (64, torch.float16, (100, 40)),
+                                          (128, torch.float16, (-1, -1)), (64, torch.bfloat16, (-1, 0))])
+def test_bwd_masked_packed_many_key_blocks(d, dt, window):
+    """Eight packed sequences of ragged, unequal lengths (empty ones included) on 16 K/V
+    heads: over a thousand 128-key blocks, windows cutting through steps and key blocks,
+    both head sizes and dtypes; the oracle checks the first and the last K/V head with
+    their query heads whole."""
+    lq, lk = [2100, 0, 1, 513, 1999, 256, 700, 1030], [2100, 5, 0, 600, 1999, 255, 900, 1030]
+    Hq, Hkv = 32, 16
+    G = Hq // Hkv
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q, k, v = _rand(9660, (Hq, cq[-1], d), dt), _rand(9661, (Hkv, ck[-1], d), dt), _rand(9662, (Hkv, ck[-1], d), dt)
+    do = _rand(9663, (Hq, cq[-1], d), dt)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    say(f"[bwd masked many key blocks] packed {len(lq)} sequences Hq={Hq} Hkv={Hkv} d={d} {dt} window={window}")
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    o, lse = fa.fwd_masked(qd, kd, vd, window, scale, cqd, ckd, max(lq), max(lk))
+    dq, dk, dv = fa.bwd_masked(qd, kd, vd, o, lse, dod, window, scale, cqd, ckd, max(lq), max(lk))
+    torch.cuda.synchronize()
+    for hk in (0, Hkv - 1):
+        hs = slice(hk * G, (hk + 1) * G)
+        ref = om.attention_bwd_masked(q[hs], k[hk:hk + 1], v[hk:hk + 1], do[hs], scale, cq, ck, window)
+        empty_q = np.zeros((G, cq[-1], d), dtype=bool)
+        unseen_k = np.zeros((1, ck[-1], d), dtype=bool)
+        for b in range(len(lq)):
+            vis = om.visible(lq[b], lk[b], window)
+            empty_q[:, cq[b]:cq[b + 1]] = (~vis.any(axis=1))[None, :, None]
+            unseen_k[:, ck[b]:ck[b + 1]] = (~vis.any(axis=0))[None, :, None]
+        _check_grads((dq[hs], dk[hk:hk + 1], dv[hk:hk + 1]), ref, empty_q, unseen_k, label=f"K/V head {hk}")
+
+
 @pytest.mark.parametrize("name", [workloads.MASK_HEADLINE, "varlen_b8_hq32_hkv8_d128_bf16_causal",
                                   "bsparse_b1_hq16_hkv4_n8192_d128_bf16"])
 def test_bwd_mask_workloads_full_size_sampled_heads(name):
