@@ -1,0 +1,60 @@
+"""The forward and backward captured in one HIP graph (torch.cuda.CUDAGraph on the
+capture stream): the library allocates nothing and clears nothing with memsets, so its
+launches record as plain kernel nodes.  Each case replays the graph several times; before
+every replay the captured inputs are rewritten in place and the same calls run eagerly
+(with synchronisations between), and every replay must equal the eager result bit for
+bit: O, LSE, dQ, dK, dV.  The shapes cover the dK/dV pass with 64 and with 32 keys a
+wave, unsplit and split with its reduction, and head size 64 in fp16.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import workloads
+from tests.gpu_util import say
+import exact_io_aware_fwd_amd as fa
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dt,causal", [
+    (4, 16, 16, 2100, 128, torch.bfloat16, True),   # 64 keys a wave, unsplit
+    (1, 32, 8, 8192, 128, torch.bfloat16, True),    # 64 keys a wave, key blocks split in two + reduction
+    (1, 16, 16, 2048, 128, torch.bfloat16, True),   # 32 keys a wave, split in two + reduction
+    (1, 8, 2, 700, 64, torch.float16, False),       # d = 64, ragged tail
+])
+def test_fwd_bwd_graph_replays_equal_eager(B, Hq, Hkv, N, d, dt, causal):
+    dev = torch.device("cuda:0")
+    say(f"[graph] fwd+bwd captured: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} {dt} causal={causal}")
+    shapes = ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, Hq, N, d))
+    q, k, v, do = (workloads.randn(700 + i, s, dt).to(dev) for i, s in enumerate(shapes))
+    ws = torch.empty(max(fa.bwd_workspace_size(B, Hq, Hkv, N, d, dt, causal), 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        return (o, lse) + fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws)
+
+    side = torch.cuda.Stream(dev)   # warm-up off the default stream, as capture requires
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = step()
+    torch.cuda.synchronize()
+
+    for r in range(3):
+        for i, t in enumerate((q, k, v, do)):
+            t.copy_(workloads.randn(800 + 10 * r + i, tuple(t.shape), dt).to(dev))
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in step()]
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), captured, eager):
+            assert torch.equal(x, y), f"replay {r}: {name} differs from the eager call"
+    del g
