@@ -12,7 +12,7 @@
 // tile follows the section "FlashAttention-3" (matmul/softmax interleaving),
 // realised here inside each wave's instruction stream.
 //
-// gfx950 design.  Two kernels share tiles, layouts and arithmetic:
+// gfx950 design.  Two kernels share tiles, layouts and the epilogue:
 //  * fwd_unit_kernel (fa_fwd): NW waves x 32 query rows, each wave taking one 32-key
 //    unit at a time while the other waves on its SIMD overlap its softmax with their
 //    products: at d = 128 12 waves (one workgroup per CU, three waves per SIMD), or 6
@@ -40,15 +40,21 @@
 //    (measured free of bank conflicts), and every LDS address is a lane
 //    constant plus an immediate.  The loads use buffer descriptors that end at
 //    row N, so rows past the sequence end land as zeros.
-//  * Scores are kept in log2 units.  The reference max is raised only when a
-//    row's max exceeds it by more than 8 (so P <= 256), and O is rescaled only
-//    when some lane of the wave raised it.
+//  * Scores are kept in log2 units.  fwd_kernel raises the reference max only when a
+//    row's max exceeds it by more than 8 (so P <= 256), and rescales O only when
+//    some lane of the wave raised it.  fwd_unit_kernel forms no row max at all on its
+//    common path: P comes from the reference as it stands, and only when a lane's
+//    probabilities over the unit sum past 256 (or the lane has no reference yet)
+//    does the wave take the row max, raise the reference and form P again; its
+//    products run at raised wave priority (s_setprio), so a wave entering them is
+//    issued ahead of waves still in their softmax.
 //  * Causal: a workgroup stops at the last tile its rows can see; units no query of a
 //    wave sees are skipped by that wave (fwd_unit_kernel) or add only zeros in a
 //    masked variant without branches (fwd_kernel).
 //  * Block ids are remapped so that all query blocks sharing a K/V head run on
 //    one XCD (block ids are dealt round-robin over the 8 XCDs) and the longest
 //    causal blocks start first.
+#include <cfloat>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -463,19 +469,18 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 }
 
 // The forward without block lists: NW waves of 32 queries, each taking one 32-key
-// unit at a time — scores, mask, reference max, exponentials and row sum, then
-// O^T += V^T P^T — with no software pipeline: the other waves on the SIMD overlap one
-// wave's softmax with their products.  Without the pipeline's second unit a wave needs
-// ~150 registers at d = 128 (three waves per SIMD) and ~90 at d = 64 (four); two
-// waves per SIMD with the same code run slower than the pipelined kernel above, three
-// and four faster.  Below 12 waves (6 at d = 128, 8 at d = 64) two LDS slots (75 KB at
-// d = 128, 43 KB at d = 64) leave room for a second workgroup per CU; at 12 three
-// slots keep two tiles in flight.  Same
-// tiles, loads, layouts, rescaling threshold and epilogue as fwd_kernel, and the same
-// arithmetic in the same order, at every NW; a unit that no query of a wave sees
-// (past its diagonal, outside its window) is skipped by that wave, which changes no
-// bit.  GEN: the mask family without block lists (lengths, packed batches, windows)
-// as in fwd_kernel.
+// unit at a time — scores, mask, exponentials and row sum (the reference max only on
+// the rare slow path), then O^T += V^T P^T at raised wave priority — with no software
+// pipeline: the other waves on the SIMD overlap one wave's softmax with their
+// products.  Without the pipeline's second unit a wave needs ~156 registers at d = 128
+// (three waves per SIMD) and ~105 at d = 64 (four).  Below 12 waves (6 at d = 128, 8
+// at d = 64) two LDS slots (75 KB at d = 128, 43 KB at d = 64) leave room for a
+// second workgroup per CU; at 12 three slots keep two tiles in flight.  Same tiles,
+// loads, layouts and epilogue as fwd_kernel; the reference max is kept differently
+// (above), so the two kernels agree to rounding, not bit for bit.  The arithmetic is
+// the same at every NW, and a unit that no query of a wave sees (past its diagonal,
+// outside its window) is skipped by that wave, which changes no bit.  GEN: the mask
+// family without block lists (lengths, packed batches, windows) as in fwd_kernel.
 template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4)))
 fwd_unit_kernel(const FwdArgs a) {
@@ -491,7 +496,7 @@ fwd_unit_kernel(const FwdArgs a) {
   constexpr int IPW = Tiles::IPW;
   constexpr int NE = D / 32;
   constexpr int NS = D / 16;
-  constexpr float TAU = 8.f;
+  constexpr float TAU_SUM = 256.f;   // bound on a lane's sum of P over a unit (2^8)
   // NSL LDS slots as distinct objects (see fwd_kernel): three with one workgroup per
   // CU, two where a second workgroup has to fit beside it
   constexpr int NSL = NW >= 12 ? 3 : 2;
@@ -581,7 +586,7 @@ fwd_unit_kernel(const FwdArgs a) {
     return cat(lds_read_tr(p + 16 * h * PV + 64 * e), lds_read_tr(p + (16 * h + 8) * PV + 64 * e));
   };
   const float c2 = a.scale_log2;
-  float mr = -INFINITY, l_run = 0.f;
+  float mr = -FLT_MAX, l_run = 0.f;   // reference (log2 units); -FLT_MAX: none yet
   f32x16 o[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e)
@@ -610,35 +615,47 @@ fwd_unit_kernel(const FwdArgs a) {
         if (oo >= lim || (GEN && oo < llo)) s[v] = -INFINITY;
       }
     }
-    float mx = s[0];
+    // P from the reference as it stands, with no row max: any reference gives the same
+    // normalised result, it only has to keep P from overflowing.  If this lane's
+    // probabilities sum past 2^TAU (so some P may exceed 2^TAU, or the lane has no
+    // reference yet, whose sentinel -FLT_MAX makes every visible P infinite), the wave
+    // takes the slow path: the row max of the unit, the reference raised to it, O and
+    // the row sum rescaled, P formed again.  Masked scores (-inf) give P = 0 either way.
+    float p[16];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    mx = half_max(mx) * c2;
-    // the reference max moves only when a row's max passes it by TAU (log2 units)
-    const bool raise = mx > mr + TAU;
-    const float mnew = raise ? mx : mr;
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    // alpha = 2^(m_old - m_new) is exactly 1 on every lane when no lane of the wave moved
-    // its reference (a lane whose reference is still -inf has l = 0, where alpha does not
-    // matter), so it is formed only when some lane did
-    float alpha = 1.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      alpha = (mr == -INFINITY) ? 0.f : fast_exp2(mr - mnew);
+    for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(s[v], c2, -mr));
+    auto rowsum = [&]() __attribute__((always_inline)) {
+      float t[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) t[v] = p[2 * v] + p[2 * v + 1];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] = t[2 * v] + t[2 * v + 1];
+      return (t[0] + t[1]) + (t[2] + t[3]);
+    };
+    float rs = rowsum();
+    if (__builtin_amdgcn_ballot_w64(!(rs <= TAU_SUM)) != 0) {
+      float mx = s[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+      const float mnew = fmaxf(mr, half_max(mx) * c2);
+      const float alpha = fast_exp2(mr - mnew);   // 0 from the sentinel, 1 if unmoved
 #pragma unroll
       for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
+      l_run *= alpha;
+      mr = mnew;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(s[v], c2, -mr));
+      rs = rowsum();
     }
-    mr = mnew;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = fast_exp2(fmaf(s[v], c2, -mref));
-    float rs = s[0];   // (not 0 + s[0]: P is never -0, so the same value, one add less)
-#pragma unroll
-    for (int v = 1; v < 16; ++v) rs += s[v];
-    l_run = fmaf(l_run, alpha, rs);
+    l_run += rs;
     const u32x4 pf[2] = {
-        u32x4{E::pack(s[0], s[1]), E::pack(s[2], s[3]), E::pack(s[4], s[5]), E::pack(s[6], s[7])},
-        u32x4{E::pack(s[8], s[9]), E::pack(s[10], s[11]), E::pack(s[12], s[13]), E::pack(s[14], s[15])}};
+        u32x4{E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]), E::pack(p[6], p[7])},
+        u32x4{E::pack(p[8], p[9]), E::pack(p[10], p[11]), E::pack(p[12], p[13]), E::pack(p[14], p[15])}};
+    // the products go first on the SIMD: a wave entering them takes the issue slots from
+    // waves still in their softmax, which keeps the matrix core fed
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2 * NE; ++k) {
       const int t = k / NE, e = k % NE;
@@ -646,6 +663,7 @@ fwd_unit_kernel(const FwdArgs a) {
       if (k + 1 < 2 * NE) vf = vread(sl, h, (k + 1) / NE, (k + 1) % NE);
       o[e] = E::mma(vc, pf[t], o[e]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   auto dma = [&](int j, unsigned char* sl) __attribute__((always_inline)) {
     Tiles::load(Kg, Vg, Lk, t_lo + j, wave, doff, sl);
