@@ -70,17 +70,17 @@ def parse():
     return p.parse_args()
 
 
+# Sources whose text decides what a pass launches: its kernels, the shared device headers,
+# and the host side that picks launch shapes and plans (fa_api.cpp, fa_internal.h).
+_SHARED_SOURCES = ["exact_io_aware_fwd_amd/csrc/fa_device.h", "exact_io_aware_fwd_amd/csrc/fa_tiles.h",
+                   "exact_io_aware_fwd_amd/csrc/fa_internal.h", "exact_io_aware_fwd_amd/csrc/fa_api.cpp"]
 KERNEL_SOURCES = {
-    "fwd": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
-            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
-    "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
-            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
-    "decode": ["exact_io_aware_fwd_amd/csrc/fa_decode.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
-               "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
-    "masks": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
-              "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
-    "fp8": ["exact_io_aware_fwd_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_fwd_amd/csrc/fa_device.h",
-            "exact_io_aware_fwd_amd/csrc/fa_tiles.h"],
+    "fwd": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip"] + _SHARED_SOURCES,
+    "bwd": ["exact_io_aware_fwd_amd/csrc/fa_bwd.hip"] + _SHARED_SOURCES,
+    "decode": ["exact_io_aware_fwd_amd/csrc/fa_decode.hip"] + _SHARED_SOURCES,
+    "masks": ["exact_io_aware_fwd_amd/csrc/fa_fwd.hip"] + _SHARED_SOURCES,
+    "fp8": ["exact_io_aware_fwd_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_fwd_amd/csrc/fa_fp8_quant.hip"]
+           + _SHARED_SOURCES,
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 1 << 30
@@ -187,8 +187,12 @@ def traffic_bytes(kind: str):
     return 1024.0 * (rec["fetch_kib"] * rec["copy_fetch_factor"] + rec["write_kib"] * rec["copy_write_factor"])
 
 
-def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
-    """The fp64 oracle on one K/V group of the workload: `heads` query heads, all N rows."""
+def cpu_baseline(w, inputs, heads: int, fwd_only: bool, gpu_out=None):
+    """The fp64 oracle on whole K/V groups of the workload: `heads` query heads of batch 0,
+    all N rows, timed.  With `gpu_out` (o, lse[, dq, dk, dv] of the same inputs, CPU
+    tensors), the oracle's results on that sample are also compared with the GPU's, at the
+    parity tests' metrics: O max error / max|O_ref|, LSE max abs error, rel-L2 of dQ, dK, dV."""
+    import numpy as np
     import oracle
     from exact_io_aware_fwd_amd import metrics
     try:
@@ -200,14 +204,16 @@ def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
     G = w.Hq // w.Hkv
     heads = max(G, min(heads, w.Hq) // G * G)        # whole K/V groups of batch 0
     qs, ks, vs, dos = q[:1, :heads], k[:1, :heads // G], v[:1, :heads // G], do[:1, :heads]
+    causal = True in w.causal
     t0 = time.perf_counter()
-    oracle.attention_fwd(qs, ks, vs, True in w.causal, w.scale)
-    flops = metrics.fwd_flops(1, heads, w.N, w.d, True in w.causal)
+    O_ref, L_ref = oracle.attention_fwd(qs, ks, vs, causal, w.scale)
+    flops = metrics.fwd_flops(1, heads, w.N, w.d, causal)
+    grads = None
     if not fwd_only:
-        oracle.attention_bwd(qs, ks, vs, dos, True in w.causal, w.scale)
-        flops += metrics.bwd_flops(1, heads, w.N, w.d, True in w.causal)
+        grads = oracle.attention_bwd(qs, ks, vs, dos, causal, w.scale)
+        flops += metrics.bwd_flops(1, heads, w.N, w.d, causal)
     dt = time.perf_counter() - t0
-    return {
+    rec = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"batch 0, query heads 0-{heads - 1} with their K/V heads, all {w.N} rows, "
                   f"{'forward' if fwd_only else 'forward + backward'} in numpy float64 "
@@ -215,6 +221,22 @@ def cpu_baseline(w, inputs, heads: int, fwd_only: bool):
                   f"{dt:.1f} s",
         "seconds": dt,
     }
+    if gpu_out is not None:
+        def f64(t):
+            return t.double().numpy()
+        o, lse = f64(gpu_out[0][:1, :heads]), f64(gpu_out[1][:1, :heads])
+        par = {"sample": f"batch 0, query heads 0-{heads - 1}",
+               "o_max_rel": float(np.max(np.abs(o - O_ref)) / np.max(np.abs(O_ref))),
+               "lse_max_abs": float(np.max(np.abs(lse - L_ref)))}
+        if grads is not None and len(gpu_out) == 5:
+            for name, x, r in zip(("dq", "dk", "dv"), (gpu_out[2][:1, :heads], gpu_out[3][:1, :heads // G],
+                                                      gpu_out[4][:1, :heads // G]), grads):
+                par[f"{name}_rel_l2"] = float(np.linalg.norm((f64(x) - r).ravel()) / np.linalg.norm(r.ravel()))
+        tol = {"o_max_rel": 1.5e-2 if w.dtype == "bf16" else 2e-3, "lse_max_abs": 1e-4,
+               "dq_rel_l2": 1e-2, "dk_rel_l2": 1e-2, "dv_rel_l2": 1e-2}
+        par["within_tolerance"] = all(par[n] <= t for n, t in tol.items() if n in par)
+        rec["parity"] = par
+    return rec
 
 
 def bench_decode(args):
@@ -619,26 +641,36 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    fwd_t = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_t = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    fwd_ms, bwd_ms = sum(fwd_t) / args.steps, sum(bwd_t) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     f_fwd = metrics.fwd_flops(w.B, w.Hq, w.N, w.d, causal)
     f_bwd = 0.0 if args.fwd_only else metrics.bwd_flops(w.B, w.Hq, w.N, w.d, causal)
     peak = metrics.MFMA_BF16_TFLOPS
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
-    passes = {"fwd": {"kernel": "fwd_unit_kernel", "launches": 1, "ms": fwd_ms,
-                      "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12}}
+    def med(t):
+        return 0.5 * (t[(len(t) - 1) // 2] + t[len(t) // 2])
+
+    # per pass: mean (the roofline figure), median and min of the per-step event times;
+    # tflops and frac from the mean, tflops_median from the median
+    passes = {"fwd": {"kernel": "fwd_unit_kernel", "launches": 1, "ms": fwd_ms, "median_ms": med(fwd_t),
+                      "min_ms": fwd_t[0], "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+                      "tflops_median": f_fwd / (med(fwd_t) * 1e-3) / 1e12}}
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
     if not args.fwd_only:
         dkdv, nl = _dkdv_kernels(w.B, w.Hq, w.Hkv, w.N, causal)
         passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_dq_kernel + " + dkdv, "launches": nl,
-                         "ms": bwd_ms, "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12}
+                         "ms": bwd_ms, "median_ms": med(bwd_t), "min_ms": bwd_t[0],
+                         "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+                         "tflops_median": f_bwd / (med(bwd_t) * 1e-3) / 1e12}
         passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
     def roofline(kind):
         return {"bound": "mfma", "achieved": passes[kind]["tflops"], "peak": peak, "unit": "TFLOP/s",
                 "frac": passes[kind]["frac"], "traffic": traffic_bytes(kind), "kernel": passes[kind]["kernel"],
                 "per_launch_flops": f_fwd if kind == "fwd" else f_bwd, "avg_ms": passes[kind]["ms"],
+                "median_ms": passes[kind]["median_ms"], "min_ms": passes[kind]["min_ms"],
                 "algorithmic_bytes": (metrics.fwd_bytes if kind == "fwd" else metrics.bwd_bytes)(
                     w.B, w.Hq, w.Hkv, w.N, w.d, 2)}
     dom = max(passes, key=lambda n: passes[n]["ms"])
@@ -659,7 +691,14 @@ def main():
         "passes": passes,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_heads, args.fwd_only)
+        # one more step outside the timed region, whose outputs the oracle checks
+        o_chk, lse_chk = fa.fwd(q, k, v, causal=causal, softmax_scale=w.scale)
+        outs = [o_chk, lse_chk]
+        if not args.fwd_only:
+            outs += list(fa.bwd(q, k, v, o_chk, lse_chk, do, causal=causal, softmax_scale=w.scale, workspace=ws))
+        torch.cuda.synchronize()
+        outs = [t[:1].cpu() for t in outs]
+        rec["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_heads, args.fwd_only, outs)
     print(json.dumps(rec), flush=True)
 
 

@@ -389,6 +389,35 @@ def _check_lists(block_cnt, block_idx, B: int, mq: int, mk: int, dev) -> int:
     return bh
 
 
+def _masked_geometry(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, dev):
+    """Sizes of a mask-family call, with the layout checks both passes make before the ABI:
+    (B, Hq, Hkv, Nq, Nk, d, longest query length, longest key length, LSE shape)."""
+    if cu_seqlens_q is not None:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+            raise ValueError("packed q, k, v must be [H, total, d] with k.shape == v.shape")
+        Hq, Nq, d = q.shape
+        Hkv, Nk = k.shape[0], k.shape[1]
+        if k.shape[2] != d:
+            raise ValueError("packed k, v must be [Hkv, total_k, d] matching q")
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k is None or cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_k must have B+1 entries like cu_seqlens_q")
+        for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+            _check(t, n, dev, torch.int32)
+        mq = Nq if max_seqlen_q is None else int(max_seqlen_q)
+        mk = Nk if max_seqlen_k is None else int(max_seqlen_k)
+        return B, Hq, Hkv, Nq, Nk, d, mq, mk, (Hq, Nq)
+    if cu_seqlens_k is not None:
+        raise ValueError("cu_seqlens_k given without cu_seqlens_q")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] with k.shape == v.shape")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must be [B, Hkv, Nk, d] matching q")
+    return B, Hq, Hkv, Nq, Nk, d, Nq, Nk, (B, Hq, Nq)
+
+
 def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, block_cnt=None, block_idx=None,
                out=None, lse=None):
@@ -400,30 +429,9 @@ def fwd_masked(q, k, v, window=(-1, -1), softmax_scale: float | None = None, cu_
     block_cnt/block_idx: int32 GPU tensors from block_lists_to_tensors, or None.
     """
     L = load()
-    packed = cu_seqlens_q is not None
     dev = q.device
-    if packed:
-        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
-            raise ValueError("packed q, k, v must be [H, total, d] with k.shape == v.shape")
-        Hq, Nq, d = q.shape
-        Hkv, Nk = k.shape[0], k.shape[1]
-        B = cu_seqlens_q.numel() - 1
-        if cu_seqlens_k is None or cu_seqlens_k.numel() != B + 1:
-            raise ValueError("cu_seqlens_k must have B+1 entries like cu_seqlens_q")
-        for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
-            _check(t, n, dev, torch.int32)
-        mq = Nq if max_seqlen_q is None else int(max_seqlen_q)
-        mk = Nk if max_seqlen_k is None else int(max_seqlen_k)
-        lse_shape = (Hq, Nq)
-    else:
-        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
-            raise ValueError("q, k, v must be [B, H, N, d] with k.shape == v.shape")
-        B, Hq, Nq, d = q.shape
-        Hkv, Nk = k.shape[1], k.shape[2]
-        if k.shape[0] != B or k.shape[3] != d:
-            raise ValueError("k, v must be [B, Hkv, Nk, d] matching q")
-        mq, mk = Nq, Nk
-        lse_shape = (B, Hq, Nq)
+    B, Hq, Hkv, Nq, Nk, d, mq, mk, lse_shape = _masked_geometry(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                                                max_seqlen_k, dev)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, dev, q.dtype)
     bh = _check_lists(block_cnt, block_idx, B, mq, mk, dev)
@@ -451,29 +459,19 @@ def bwd_masked(q, k, v, o, lse, do, window=(-1, -1), softmax_scale: float | None
     """dQ, dK, dV under the mask family via fa_bwd_masked (layouts and block lists as in
     fwd_masked)."""
     L = load()
-    packed = cu_seqlens_q is not None
     dev = q.device
-    if packed:
-        Hq, Nq, d = q.shape
-        Hkv, Nk = k.shape[0], k.shape[1]
-        B = cu_seqlens_q.numel() - 1
-        mq = Nq if max_seqlen_q is None else int(max_seqlen_q)
-        mk = Nk if max_seqlen_k is None else int(max_seqlen_k)
-        for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
-            _check(t, n, dev, torch.int32)
-    else:
-        B, Hq, Nq, d = q.shape
-        Hkv, Nk = k.shape[1], k.shape[2]
-        mq, mk = Nq, Nk
+    B, Hq, Hkv, Nq, Nk, d, mq, mk, lse_shape = _masked_geometry(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                                                max_seqlen_k, dev)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check(t, n, dev, q.dtype)
     _check(lse, "lse", dev, torch.float32)
-    if o.shape != q.shape or do.shape != q.shape or k.shape != v.shape:
-        raise ValueError("o and do must match q; k and v must match")
+    if o.shape != q.shape or do.shape != q.shape or tuple(lse.shape) != lse_shape:
+        raise ValueError("o and do must match q, and lse must be " + str(lse_shape))
     bh = _check_lists(block_cnt, block_idx, B, mq, mk, dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     need = L.fa_bwd_masked_workspace_size(B, Hq, Hkv, mq, mk, int(block_idx is not None))
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _check(ws, "workspace", dev)
     dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
     ptr = lambda t: None if t is None else t.data_ptr()
     with torch.cuda.device(dev):

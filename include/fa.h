@@ -285,10 +285,24 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float
                      int64_t d, int64_t block_q, int64_t block_kv, int causal, float softmax_scale,
                      struct ihipStream_t* stream);
 
-/* Static, human-readable name of a status code. */
+/*
+ * Error reporting.  The "Flash Attention" wiki (sections "Framework integration" and
+ * "Specialized kernels have boundaries") describes fused kernels that reject inputs
+ * outside their specialisation, and a forced backend that turns an unsupported call into
+ * an error instead of quietly running another kernel.  This library does the same: a
+ * call it cannot serve returns a status and runs nothing; there is no fallback.  These
+ * two functions let the caller report why.
+ *
+ * fa_status_string: static, human-readable name of a status code ("FA_ERR_UNKNOWN" for
+ * a value outside the enum).  The string is owned by the library and never freed.
+ *
+ * fa_last_error: detail text of the last failed call made on the calling thread ("" if
+ * none has failed since the thread started; a successful call leaves it unchanged).  The
+ * buffer is thread-local and owned by the library: the pointer stays valid for the
+ * thread's life, and the next failed call on that thread overwrites its contents.
+ */
 const char* fa_status_string(fa_status s);
 
-/* Thread-local detail text of the last failed call on this thread ("" if none). */
 const char* fa_last_error(void);
 
 #ifdef __cplusplus

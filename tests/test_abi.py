@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from exact_io_aware_fwd_amd import binding
+from tests.bwd_plan import dense_plan as _dense_plan
 
 OK, INV, UNS = binding.FA_OK, binding.FA_ERR_INVALID_ARGUMENT, binding.FA_ERR_UNSUPPORTED
 P = 0x10000          # an aligned fake device address (never dereferenced here)
@@ -100,23 +101,6 @@ def test_bwd_workspace_too_small(L):
     assert "workspace" in binding.last_error()
 
 
-def _dense_plan(B, Hq, Hkv, N, causal):
-    """fa_bwd's dK/dV records (256 or 128 keys) and chunks per record: chunks enough to give
-    the CUs 256 (512 when causal) workgroups, at most 16, each at least 32 query steps of the
-    longest record (256 for 256-key records); 256-key records when they reach that alone or
-    give as many workgroups."""
-    steps = (Hq // Hkv) * -(-N // 32)
-    target = 512 if causal else 256
-
-    def chunks(r, m):
-        return max(min(target // r, 16, steps // m), 1)
-
-    r256, r128 = B * Hkv * -(-N // 256), B * Hkv * -(-N // 128)
-    if r256 >= target or r256 * chunks(r256, 256) >= r128 * chunks(r128, 32):
-        return 256, chunks(r256, 256)
-    return 128, chunks(r128, 32)
-
-
 def test_workspace_size_values(L):
     # two fp32 row terms (LSE*log2e, -D) per query row, rows padded to 32 per head; with few
     # key blocks, then the partial dK/dV slots of the split key blocks from a 256-byte boundary
@@ -142,6 +126,30 @@ def test_python_binding_validates_before_the_abi():
         binding.fwd(q, q, q)          # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         binding._dtype_code(torch.zeros(1, dtype=torch.float32))
+
+
+def test_masked_bindings_check_layouts_before_the_abi():
+    """Both mask-family bindings parse the layout (packed [H, total, d] with cumulative
+    lengths, or [B, H, N, d]) before anything reaches the library, and refuse a workspace
+    that is not a GPU tensor."""
+    import torch
+    q4 = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    q3 = torch.zeros(2, 16, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 16)
+    cu = torch.tensor([0, 16], dtype=torch.int32)
+    for args in ((q4, q4, q4), (q3, q3, q3)):
+        packed = args[0].dim() == 4      # the wrong layout for the cumulative-length argument
+        kw = {"cu_seqlens_q": cu, "cu_seqlens_k": cu} if packed else {}
+        with pytest.raises(ValueError):
+            binding.fwd_masked(*args, **kw)
+        with pytest.raises(ValueError):
+            binding.bwd_masked(*args, args[0], lse, args[0], **kw)
+    with pytest.raises(ValueError):      # k and v of different shapes
+        binding.bwd_masked(q4, q4, torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16), q4, lse, q4)
+    with pytest.raises(ValueError):      # cumulative key lengths of the wrong count
+        binding.fwd_masked(q3, q3, q3, cu_seqlens_q=cu, cu_seqlens_k=torch.tensor([0, 8, 16], dtype=torch.int32))
+    with pytest.raises(ValueError):      # the device check every workspace goes through
+        binding._check(torch.zeros(64, dtype=torch.uint8), "workspace", torch.device("cuda:0"))
 
 
 def splitkv(L, ws_bytes=1 << 24, B=1, Hq=8, Hkv=2, Nq=1, Nk=100, d=128, dtype=1, causal=0, scale=0.125, S=0,

@@ -118,7 +118,8 @@ def test_dq_workgroup_shape_does_not_change_bits(causal, hq):
         assert rel_l2(dq_big[:, h:h + 1].cpu(), dQ) <= GRAD_TOL
 
 
-@pytest.mark.parametrize("d,dt", [(64, torch.float16), (128, torch.float16), (64, torch.bfloat16)])
+@pytest.mark.parametrize("d,dt", [(64, torch.float16), (128, torch.float16), (64, torch.bfloat16),
+                                  (128, torch.bfloat16)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dkdv_64_key_waves_sampled_heads(d, dt, causal):
     """4 x 16 heads of 2100 tokens give 576 blocks of 256 keys, so the dK/dV pass runs 64

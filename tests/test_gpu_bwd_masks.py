@@ -339,3 +339,26 @@ def test_bwd_masked_inconsistent_lists_stay_in_bounds():
         torch.cuda.synchronize()
         for t in grads:
             assert torch.isfinite(t.float()).all()
+
+
+def test_bwd_masked_refuses_a_host_workspace_and_a_short_lse():
+    """The binding checks the caller's workspace (a GPU tensor on q's device) and the LSE
+    shape ([Hq, total] packed, [B, Hq, N] fixed) before the ABI call: a host pointer or a
+    short LSE would otherwise reach the kernels."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 200, 64
+    q, k, v, do = to_dev(_rand(9990, (B, Hq, N, d)), _rand(9991, (B, Hkv, N, d)), _rand(9992, (B, Hkv, N, d)),
+                         _rand(9993, (B, Hq, N, d)))
+    o, lse = fa.fwd_masked(q, k, v, (-1, 0))
+    torch.cuda.synchronize()
+    say("[bwd masked] host workspace and short LSE are refused")
+    with pytest.raises(ValueError):
+        fa.bwd_masked(q, k, v, o, lse, do, (-1, 0), workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        fa.bwd_masked(q, k, v, o, lse[:, :, :-1].contiguous(), do, (-1, 0))
+    qp, kp, vp, op, dop = (t[0] for t in (q, k, v, o, do))        # packed: one sequence of N
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda:0")
+    with pytest.raises(ValueError):
+        fa.bwd_masked(qp, kp, vp, op, lse, dop, (-1, 0), cu_seqlens_q=cu, cu_seqlens_k=cu)   # lse not [Hq, N]
+    dq = fa.bwd_masked(qp, kp, vp, op, lse[0], dop, (-1, 0), cu_seqlens_q=cu, cu_seqlens_k=cu)[0]
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all()

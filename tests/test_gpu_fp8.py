@@ -44,7 +44,7 @@ import exact_io_aware_fwd_amd as fa
 
 pytestmark = pytest.mark.gpu
 
-EPS = 2.0 ** -11     # accumulation error bound of the FP8 matrix product (see above)
+EPS = 2.0 ** -11     # accumulation error bound of the FP8 matrix product (see above and the test below)
 
 
 def _perm():
@@ -274,3 +274,42 @@ def test_fp8_exact_inputs_match_exact_attention():
     O, L = oracle.attention_fwd(q, k, v, True, 0.125)
     O2, L2 = ofp8.attention_fwd_fp8(q, k, v, None, True, 0.125)
     assert np.max(np.abs(O - O2)) < 1e-12 and np.max(np.abs(L - L2)) < 1e-12
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_product_error_within_half_eps(d):
+    """The measurement behind EPS.  With one key and one query per head, the forward's LSE
+    is the score itself, S = scale * q.k, formed by the scaled FP8 matrix product (one
+    64-deep product at d = 64; at d = 128 two, the first result being the second's
+    accumulator input), so |LSE - S_exact| is that product's accumulation error.  The
+    operands are block-quantised values whose magnitudes span 2^-8 .. 2^8 (every e4m3
+    binade, subnormals included) with random signs (sums with heavy cancellation), 4096
+    heads per case.  Each product is held to EPS / 2 of the magnitudes it sums (its
+    products and its accumulator input), the per-product error the derivation above
+    doubles for its margin; fp32 rounding of LSE = ln 2 * (S log2 e) is allowed on top."""
+    B, H = 64, 64
+    g = np.random.Generator(np.random.PCG64(9800 + d))
+
+    def draw():
+        mag = np.exp2(g.uniform(-8.0, 8.0, (B, H, 1, d)))
+        sign = np.where(g.random((B, H, 1, d)) < 0.5, -1.0, 1.0)
+        return torch.from_numpy((mag * sign).astype(np.float32)).to(torch.bfloat16)
+
+    q, k = draw(), draw()
+    v = workloads.randn(9810 + d, (B, H, 1, d), torch.bfloat16)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    say(f"[fp8 fwd] score product error, d={d}, {B * H} single-key heads")
+    _, lse = _run_gpu(q, k, v, None, True, scale, 64, 64)
+    Qh, Kh, _ = ofp8.quantized_operands(q, k, v, None, 64, 64)
+    prod = scale * Qh[:, :, 0, :] * Kh[:, :, 0, :]                 # [B, H, d], exact in float64
+    S = prod.sum(axis=-1)
+    a1 = np.abs(prod[..., :64]).sum(axis=-1)
+    a2 = np.abs(prod[..., 64:]).sum(axis=-1)
+    # per product EPS/2 of (its products + its accumulator input, |first result| <= a1)
+    bound = EPS / 2 * (a1 + a2 + (a1 if d == 128 else 0.0)) + 8 * 2.0 ** -24 * np.abs(S) + 1e-30
+    err = np.abs(lse[:, :, 0] - S)
+    rel = err / (a1 + a2)
+    say(f"    max |LSE - S| / sum|products| = {rel.max():.3e} (2^{np.log2(max(rel.max(), 1e-30)):.2f}); "
+        f"mean {rel.mean():.3e}; per-product bound EPS/2 = 2^{np.log2(EPS / 2):.0f}")
+    assert np.all(np.isfinite(lse)), "non-finite LSE"
+    assert np.all(err <= bound), f"accumulation error above EPS/2 per product: worst {np.max(err / bound):.3f}x"
