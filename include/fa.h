@@ -296,10 +296,10 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float
  * fa_status_string: static, human-readable name of a status code ("FA_ERR_UNKNOWN" for
  * a value outside the enum).  The string is owned by the library and never freed.
  *
- * fa_last_error: detail text of the last failed call made on the calling thread ("" if
- * none has failed since the thread started; a successful call leaves it unchanged).  The
- * buffer is thread-local and owned by the library: the pointer stays valid for the
- * thread's life, and the next failed call on that thread overwrites its contents.
+ * fa_last_error: detail text of the failure of the most recent call on the calling thread.
+ * Every entry point that returns an fa_status clears it on entry, so it is "" after a
+ * successful call.  The buffer is thread-local and owned by the library: the pointer
+ * stays valid for the thread's life, and the next such call on that thread rewrites it.
  */
 const char* fa_status_string(fa_status s);
 
