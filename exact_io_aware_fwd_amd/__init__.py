@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     block_lists_to_tensors,
     bwd,
     bwd_masked,
+    bwd_noalloc,
     bwd_workspace_size,
     declared_symbols,
     fp8_prepare,

@@ -50,6 +50,9 @@ def load() -> ctypes.CDLL:
     L.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                          _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_float, _vp]
+    L.fa_bwd_noalloc.restype = ctypes.c_int
     L.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_float, _i64, _vp]
     L.fa_fwd_splitkv.restype = ctypes.c_int
@@ -188,6 +191,38 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None =
         st = L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
                       B, Hq, Hkv, N, d, _dtype_code(q), int(bool(causal)), scale, stream)
+    if st != FA_OK:
+        _raise(st)
+    return dq, dk, dv
+
+
+# Bytes of the static device scratch behind fa_bwd_noalloc (include/fa.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def bwd_noalloc(q, k, v, o, lse, do, causal: bool = False, softmax_scale: float | None = None, out=None):
+    """dQ, dK, dV via fa_bwd_noalloc: fa_bwd with its workspace in the library's static
+    device scratch (no workspace argument; calls that overlap on one GPU race).  `out`
+    optionally gives preallocated (dq, dk, dv)."""
+    L = load()
+    B, Hq, Hkv, N, d = _shapes(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, dev, q.dtype)
+    _check(lse, "lse", dev, torch.float32)
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, Hq, N):
+        raise ValueError("o/do/lse have the wrong shape")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check(t, n, dev, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} has the wrong shape")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, _dtype_code(q),
+                              int(bool(causal)), scale, stream)
     if st != FA_OK:
         _raise(st)
     return dq, dk, dv

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "fa_internal.h"
 
@@ -279,27 +280,14 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int6
   return fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype, int causal,
-                 float softmax_scale, struct ihipStream_t* stream) {
-  g_last_error[0] = '\0';
-  bool empty = false;
-  fa_status st = check_sizes(B, Hq, Hkv, N, d, dtype, &empty);
-  if (st != FA_OK) return st;
-  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
-  if (empty) return FA_OK;
-  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(k, "k")) != FA_OK ||
-      (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
-      (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(dout, "dout")) != FA_OK ||
-      (st = check_ptr(dq, "dq")) != FA_OK || (st = check_ptr(dk, "dk")) != FA_OK ||
-      (st = check_ptr(dv, "dv")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
-    return st;
-  const size_t need = fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
-  if (workspace_bytes < need)
-    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
-                need);
+namespace {
 
+// fa_bwd after argument checks common to it and fa_bwd_noalloc (the workspace pointer and
+// size are checked by the callers).
+fa_status bwd_checked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, void* workspace, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype, int causal, float softmax_scale,
+                      struct ihipStream_t* stream) {
   fa::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -324,6 +312,101 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const hipError_t err = fa::launch_bwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
   if (err != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
   return FA_OK;
+}
+
+fa_status bwd_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t N, int64_t d, fa_dtype dtype, float softmax_scale, bool* empty) {
+  fa_status st = check_sizes(B, Hq, Hkv, N, d, dtype, empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+  if (*empty) return FA_OK;
+  if ((st = check_ptr(q, "q")) != FA_OK || (st = check_ptr(k, "k")) != FA_OK ||
+      (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
+      (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(dout, "dout")) != FA_OK ||
+      (st = check_ptr(dq, "dq")) != FA_OK || (st = check_ptr(dk, "dk")) != FA_OK ||
+      (st = check_ptr(dv, "dv")) != FA_OK)
+    return st;
+  return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, fa_dtype dtype, int causal,
+                 float softmax_scale, struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, dtype, softmax_scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if ((st = check_ptr(workspace, "workspace")) != FA_OK) return st;
+  const size_t need = fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, dtype, causal, softmax_scale,
+                     stream);
+}
+
+// ---- fa_bwd_noalloc: the backward with its workspace in a static device array ----
+//
+// `scratch` is a file-scope device array: one copy per GPU, created when the code object
+// is loaded on that GPU and held until the process ends.  In host code its name is only a
+// host-side stand-in, never a device address, so the first call on each device looks up
+// that device's copy with hipGetSymbolAddress (with the device current) and keeps the
+// pointer; kernels receive only that pointer.  Nothing is allocated or freed per call.
+// The backward's workspace needs no clearing: the row-term kernel writes every row term
+// and every chunk of a split plan writes its whole partial slot, so the contents a
+// previous call left behind are overwritten before they are read.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch supports", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(err));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t N, int64_t d, fa_dtype dtype, int causal, float softmax_scale,
+                         struct ihipStream_t* stream) {
+  g_last_error[0] = '\0';
+  bool empty = false;
+  fa_status st = bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, dtype, softmax_scale, &empty);
+  if (st != FA_OK || empty) return st;
+  const size_t need = fa::bwd_dense_bytes(B, Hq, Hkv, N, d, causal != 0);
+  if (need > kScratchBytes)
+    return fail(FA_ERR_INVALID_ARGUMENT,
+                "these sizes need %zu bytes of workspace, more than the %zu bytes of static scratch "
+                "fa_bwd_noalloc has; call fa_bwd with a workspace instead",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != FA_OK) return st;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, N, d, dtype, causal, softmax_scale, stream);
 }
 
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,

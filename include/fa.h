@@ -286,6 +286,25 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float
                      struct ihipStream_t* stream);
 
 /*
+ * Backward pass without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and bits as fa_bwd minus the workspace: the
+ * workspace fa_bwd_workspace_size() reports for these sizes lives in a static device
+ * array of 64 MiB (67108864 bytes) per GPU, created when the
+ * library's code is loaded on that GPU and held until the process ends.  Nothing is
+ * allocated or freed by the call.  Sizes whose workspace exceeds that maximum return
+ * FA_ERR_INVALID_ARGUMENT (use fa_bwd).  All calls on one GPU share its array, so calls
+ * that may overlap in time on one GPU (different streams, different threads without
+ * ordering) race and give undefined results; calls in one stream are ordered and safe.
+ * The first call on each device, with that device current, looks up the array's address
+ * (hipGetSymbolAddress); a failure there returns FA_ERR_HIP.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t N, int64_t d, fa_dtype dtype, int causal, float softmax_scale,
+                         struct ihipStream_t* stream);
+
+/*
  * Error reporting.  The "Flash Attention" wiki (sections "Framework integration" and
  * "Specialized kernels have boundaries") describes fused kernels that reject inputs
  * outside their specialisation, and a forced backend that turns an unsupported call into

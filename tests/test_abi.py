@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
                           "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_num_splits",
                           "fa_lse_combine", "fa_fp8_v_codes_bytes", "fa_fp8_quantize_rows", "fa_fp8_quantize_v",
                           "fa_fwd_fp8", "fa_fwd_masked", "fa_bwd_masked",
-                          "fa_bwd_masked_workspace_size"}
+                          "fa_bwd_masked_workspace_size", "fa_bwd_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for n in names:
@@ -126,6 +126,26 @@ def test_python_binding_validates_before_the_abi():
         binding.fwd(q, q, q)          # CPU tensors are refused before any call
     with pytest.raises(TypeError):
         binding._dtype_code(torch.zeros(1, dtype=torch.float32))
+
+
+def test_bwd_noalloc_validates_on_the_host(L):
+    """fa_bwd_noalloc checks its arguments as fa_bwd does, and refuses sizes whose workspace
+    would not fit its 64 MiB static scratch, before any HIP call (so no device is touched)."""
+    def call(B=1, Hq=2, Hkv=1, N=16, d=64, dtype=1, causal=0, scale=0.125, **ptrs):
+        p = {n: ptrs.get(n, P) for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")}
+        return L.fa_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                                B, Hq, Hkv, N, d, dtype, causal, scale, None)
+    assert call(B=0) == OK and call(N=0) == OK
+    assert call(q=0) == INV and "q is NULL" in binding.last_error()
+    assert call(dv=P + 8) == INV
+    assert call(d=96) == UNS
+    assert call(Hq=3, Hkv=2) == INV
+    assert call(scale=float("nan")) == INV
+    # 8 bytes of row terms per query row: 2^23 rows plus padding exceed 64 MiB
+    B, Hq, N = 4, 64, 32768 + 32
+    assert L.fa_bwd_workspace_size(B, Hq, 8, N, 128, 1, 1) > binding.NOALLOC_SCRATCH_BYTES
+    assert call(B=B, Hq=Hq, Hkv=8, N=N, d=128, causal=1) == INV
+    assert "static scratch" in binding.last_error()
 
 
 def test_masked_bindings_check_layouts_before_the_abi():
