@@ -520,7 +520,9 @@ def bench_sweep(args):
     """Forward and backward TFLOP/s (algorithmic FLOPs / time with HIP events on the launch
     stream, best of three rounds of 10 calls each) over d in {128, 64}, (B, Hq, Hkv) in
     {(1, 16, 16), (1, 32, 8), (2, 32, 8), (4, 32, 8)}, N from 1K to 16K (at most 1M query
-    rows), causal or not; seeded N(0, 1) bf16 inputs."""
+    rows), causal or not; seeded N(0, 1) bf16 inputs, and fp16 ones at d = 128, N >= 4K.
+    The forward is timed twice: fa_fwd, and fa_fwd_splitkv with as many queries as keys
+    (the key-split route, default splits)."""
     import torch
     import workloads
     import exact_io_aware_fwd_amd as fa
@@ -545,31 +547,40 @@ def bench_sweep(args):
         return best
 
     warm_until = time.perf_counter() + 0.3    # let the clocks ramp before the first shape
-    print("| d | B | Hq/Hkv | N | causal | fa_fwd ms | fwd TFLOP/s | fa_bwd ms | bwd TFLOP/s |")
-    print("|---|---|---|---|---|---|---|---|---|", flush=True)
+    print("| d | dtype | B | Hq/Hkv | N | causal | fa_fwd ms | fwd TFLOP/s | split-KV fwd ms (splits) | "
+          "split TFLOP/s | fa_bwd ms | bwd TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|", flush=True)
     for d in (128, 64):
         for (B, Hq, Hkv) in ((1, 16, 16), (1, 32, 8), (2, 32, 8), (4, 32, 8)):
             for N in (1024, 2048, 4096, 8192, 16384):
                 if B * Hq * N > 2 * 32 * 16384:
                     continue
-                q, k, v, do = (workloads.randn(1000 + i, (B, h, N, d), torch.bfloat16).to(dev)
-                               for i, h in enumerate((Hq, Hkv, Hkv, Hq)))
-                for causal in (True, False):
-                    o = torch.empty_like(q)
-                    lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
-                    ws = torch.empty(max(fa.bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype, causal), 16),
-                                     dtype=torch.uint8, device=dev)
-                    fwd = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
-                    while time.perf_counter() < warm_until:
-                        fwd()
-                        torch.cuda.synchronize()
-                    tf = best_ms(fwd)
-                    tb = best_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws))
-                    ff = metrics.fwd_flops(B, Hq, N, d, causal)
-                    fb = metrics.bwd_flops(B, Hq, N, d, causal)
-                    print(f"| {d} | {B} | {Hq}/{Hkv} | {N} | {'yes' if causal else 'no'} | {tf:.4f} | "
-                          f"{ff / tf / 1e9:.0f} | {tb:.4f} | {fb / tb / 1e9:.0f} |", flush=True)
-                del q, k, v, do
+                # fp16 as well where the sm75 README's tables measure it at length (d = 128, N >= 4K)
+                for dt in ((torch.bfloat16, torch.float16) if d == 128 and N >= 4096 else (torch.bfloat16,)):
+                    q, k, v, do = (workloads.randn(1000 + i, (B, h, N, d), dt).to(dev)
+                                   for i, h in enumerate((Hq, Hkv, Hkv, Hq)))
+                    for causal in (True, False):
+                        o = torch.empty_like(q)
+                        lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+                        ws = torch.empty(max(fa.bwd_workspace_size(B, Hq, Hkv, N, d, q.dtype, causal), 16),
+                                         dtype=torch.uint8, device=dev)
+                        wss = torch.empty(max(fa.splitkv_workspace_size(B, Hq, Hkv, N, N, d, q.dtype), 16),
+                                          dtype=torch.uint8, device=dev)
+                        nsp = fa.splitkv_num_splits(B, Hq, Hkv, N, N, d)
+                        fwd = lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+                        while time.perf_counter() < warm_until:
+                            fwd()
+                            torch.cuda.synchronize()
+                        tf = best_ms(fwd)
+                        ts = best_ms(lambda: fa.fwd_splitkv(q, k, v, causal=causal, workspace=wss, out=o, lse=lse))
+                        tb = best_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws))
+                        ff = metrics.fwd_flops(B, Hq, N, d, causal)
+                        fb = metrics.bwd_flops(B, Hq, N, d, causal)
+                        name = {torch.bfloat16: "bf16", torch.float16: "fp16"}[dt]
+                        print(f"| {d} | {name} | {B} | {Hq}/{Hkv} | {N} | {'yes' if causal else 'no'} | {tf:.4f} | "
+                              f"{ff / tf / 1e9:.0f} | {ts:.4f} ({nsp}) | {ff / ts / 1e9:.0f} | {tb:.4f} | "
+                              f"{fb / tb / 1e9:.0f} |", flush=True)
+                    del q, k, v, do
 
 
 def main():

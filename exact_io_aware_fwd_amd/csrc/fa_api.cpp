@@ -94,6 +94,12 @@ fa_status check_splitkv_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   if (Nk == 0) return fail(FA_ERR_INVALID_ARGUMENT, "Nk = 0: the queries have no keys");
   if (causal && Nq > Nk)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal needs Nq <= Nk (Nq=%lld Nk=%lld)", (long long)Nq, (long long)Nk);
+  if (fa::splitkv_is_prefill(Nq, Nk)) {
+    const fa::PrefillSplit p = fa::plan_prefill_split(B, Hq, Nq, num_splits);
+    if (B * Hq * ((Nq + 191) / 192) * p.S > (int64_t)UINT_MAX || Nq * d > INT_MAX)
+      return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
+    return FA_OK;
+  }
   const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits);
   if ((int64_t)B * Hkv * p.RG * (p.S4 / 4) > (int64_t)UINT_MAX)
     return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
@@ -414,12 +420,15 @@ size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   bool empty = false;
   if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, dtype, 0, num_splits, &empty) != FA_OK) return 0;
   if (empty) return 0;
+  if (fa::splitkv_is_prefill(Nq, Nk))
+    return fa::prefill_workspace_bytes(B, Hq, Nq, d, fa::plan_prefill_split(B, Hq, Nq, num_splits));
   return fa::splitkv_workspace_bytes(B, Hq, Nq, d, fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits));
 }
 
 int64_t fa_fwd_splitkv_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
   bool empty = false;
   if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, FA_BF16, 0, 0, &empty) != FA_OK || empty) return 0;
+  if (fa::splitkv_is_prefill(Nq, Nk)) return fa::plan_prefill_split(B, Hq, Nq, 0).S;
   const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, 0);
   return (Nk + p.C - 1) / p.C;
 }
@@ -438,6 +447,46 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
       (st = check_ptr(v, "v")) != FA_OK || (st = check_ptr(o, "o")) != FA_OK ||
       (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
     return st;
+  if (fa::splitkv_is_prefill(Nq, Nk)) {   // as many queries as keys: key-split prefill
+    const fa::PrefillSplit p = fa::plan_prefill_split(B, Hq, Nq, num_splits);
+    const size_t need = fa::prefill_workspace_bytes(B, Hq, Nq, d, p);
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                  need);
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = (int)B;
+    a.Hq = (int)Hq;
+    a.Hkv = (int)Hkv;
+    a.N = (int)Nq;
+    a.Nk = (int)Nk;
+    a.maxq = (int)Nq;
+    a.maxk = (int)Nk;
+    a.wl = -1;
+    a.wr = causal ? 0 : -1;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * kLog2e;
+    hipError_t err;
+    if (p.S == 1) {   // one split: the forward writes O and LSE itself
+      err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
+    } else {
+      a.ksplit = p.S;
+      a.kchunk = p.C;
+      a.opart = static_cast<float*>(workspace);
+      a.lpart =
+          reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + fa::prefill_opart_bytes(B, Hq, Nq, d, p));
+      err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
+      if (err == hipSuccess)
+        err = fa::launch_lse_combine(a.opart, a.lpart, o, lse, B * Hq * Nq, p.S, (int)d, dtype == FA_BF16,
+                                     (hipStream_t)stream);
+    }
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "key-split forward launch failed: %s", hipGetErrorString(err));
+    return FA_OK;
+  }
   const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits);
   const size_t need = fa::splitkv_workspace_bytes(B, Hq, Nq, d, p);
   if (workspace_bytes < need)

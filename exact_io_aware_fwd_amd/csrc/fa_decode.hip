@@ -367,10 +367,50 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(const float* opart, co
   }
 }
 
+// The same combine for few parts (S <= 16) and many rows: D/4 threads per row, four
+// adjacent elements each (one 16-byte load per part), 256 / (D/4) rows per workgroup.
+// Every thread of a row reads the row's S statistics (the same cache lines).
+template <class Tag, int D>
+__global__ void __launch_bounds__(256) lse_combine_rows_kernel(const float* opart, const float* lpart, void* o,
+                                                               float* lse, long long rows, int S) {
+  using E = Elt<Tag>;
+  constexpr int TPR = D / 4;             // threads per row
+  const long long row = ((long long)blockIdx.y * gridDim.x + blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int e4 = (threadIdx.x % TPR) * 4;
+  const float* lp = lpart + row * S;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    const float* op = opart + row * (long long)S * D + e4;
+    for (int s = 0; s < S; ++s) {
+      const float l = lp[s];
+      if (l == -INFINITY) continue;              // empty part: its O carries no weight
+      const float w = fast_exp2((l - M) * kLog2e);
+      den += w;
+      acc += w * *(const f32x4*)(op + (long long)s * D);
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const u32x2 w = {E::pack(acc[0] * inv, acc[1] * inv), E::pack(acc[2] * inv, acc[3] * inv)};
+  *(u32x2*)((unsigned char*)o + row * (D * 2) + e4 * 2) = w;
+  if (e4 == 0) lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
+}
+
 template <class Tag, int D>
 static hipError_t launch_combine_t(const float* opart, const float* lpart, void* o, float* lse, long long rows, int S,
                                    hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (S <= 16) {
+    const long long nb = (rows + 256 / (D / 4) - 1) / (256 / (D / 4));
+    const unsigned gx = (unsigned)(nb < 65536 ? nb : 65536);
+    const unsigned gy = (unsigned)((nb + gx - 1) / gx);
+    hipLaunchKernelGGL((lse_combine_rows_kernel<Tag, D>), dim3(gx, gy), dim3(256), 0, stream, opart, lpart, o, lse,
+                       rows, S);
+    return hipGetLastError();
+  }
   const unsigned gx = (unsigned)(rows < 65536 ? rows : 65536);
   const unsigned gy = (unsigned)((rows + gx - 1) / gx);
   hipLaunchKernelGGL((lse_combine_kernel<Tag, D>), dim3(gx, gy), dim3(256), 0, stream, opart, lpart, o, lse, rows, S);

@@ -511,7 +511,10 @@ fwd_unit_kernel(const FwdArgs a) {
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
   int b, hq, iq;
-  map_q_block(((GEN ? a.maxq : N) + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  // key split: consecutive blocks are the splits of one query block
+  const int ks = GEN ? a.ksplit : 1;
+  const int sidx = ks > 1 ? (int)blockIdx.x % ks : 0;
+  map_q_block(((GEN ? a.maxq : N) + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq, (int)blockIdx.x / ks);
   const int hkv = hq / (a.Hq / a.Hkv);
   // sequence geometry: Lq queries, Lk keys (offsets clamped to the tensors)
   int Lq = N, Lk = N;
@@ -564,7 +567,18 @@ fwd_unit_kernel(const FwdArgs a) {
     uhi = qw >= Lq ? -1 : hi_of(qlw);
     wlo = max(lo_of(qlw), 0);
     whi = hi_of(qw);
-    const int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
+    int klo = max(lo_of(q0), 0), khi = hi_of(qlast);
+    if (ks > 1) {   // this split's keys only (64-key aligned, so whole units)
+      const int kb = sidx * a.kchunk, ke = min(kb + a.kchunk, Lk) - 1;
+      lo_q = max(lo_q, kb);
+      hi_q = min(hi_q, ke);
+      ulo = max(ulo, kb);
+      uhi = min(uhi, ke);
+      wlo = max(wlo, kb);
+      whi = min(whi, ke);
+      klo = max(klo, kb);
+      khi = min(khi, ke);
+    }
     t_lo = klo / BC;
     ntile = (Lk <= 0 || khi < klo) ? 0 : khi / BC + 1 - t_lo;
   } else {
@@ -702,6 +716,23 @@ fwd_unit_kernel(const FwdArgs a) {
   // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l); a row that saw no key (mask
   // family only) gets O = 0 and LSE = -inf
   const float l_tot = half_sum(l_run);
+  if (GEN && ks > 1) {   // this split's part of the row: O / l in fp32 and its LSE
+    if (myq < Lq) {
+      const float inv = !(l_tot > 0.f) ? 0.f : 1.f / l_tot;
+      const size_t part = (qhead + myq) * (size_t)ks + sidx;
+      float* op = a.opart + part * D;
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * e + 8 * g + 4 * hh;
+          *(f32x4*)(op + d0) = f32x4{o[e][4 * g] * inv, o[e][4 * g + 1] * inv, o[e][4 * g + 2] * inv,
+                                     o[e][4 * g + 3] * inv};
+        }
+      if (hh == 0) a.lpart[part] = !(l_tot > 0.f) ? -INFINITY : (mr + log2f(l_tot)) * kLn2;
+    }
+    return;
+  }
   if (myq < Lq) {
     const float inv = (GEN && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
     unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
@@ -733,9 +764,10 @@ static int fwd_unit_waves(long long rows_blocks_of_384, bool causal) {
 template <class Tag, int D, bool CAUSAL, bool GEN>
 static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStream_t stream) {
   const long long bh = (long long)a.B * a.Hq;
-  const int nw = fwd_unit_waves<D>(bh * ((nq + 383) / 384), causal);
+  const int ks = GEN ? a.ksplit : 1;   // key splits multiply the grid
+  const int nw = fwd_unit_waves<D>(bh * ((nq + 383) / 384) * ks, causal);
   const int br = 32 * nw;
-  const long long nb = bh * ((nq + br - 1) / br);
+  const long long nb = bh * ((nq + br - 1) / br) * ks;
   if (nb <= 0) return hipSuccess;
   if constexpr (D == 128) {
     if (nw == 6)

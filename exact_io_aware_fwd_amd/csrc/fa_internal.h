@@ -26,6 +26,13 @@ struct FwdArgs {
   const int* bcnt = nullptr;  // block lists: counts [B, bheads, bnq]
   const int* bidx = nullptr;  //              tiles  [B, bheads, bnq, bcap], ascending
   int bheads = 1, bnq = 0, bcap = 0;
+  // Key split (the general kernel, fixed lengths, no block lists): workgroup split s of
+  // ksplit sees only keys [s*kchunk, (s+1)*kchunk) and writes its part of every row,
+  // O / l in fp32 to opart [rows, ksplit, d] and its LSE to lpart [rows, ksplit]
+  // (rows in [B, Hq, N] order), to be merged by the LSE combine.
+  int ksplit = 1, kchunk = 0;
+  float* opart = nullptr;
+  float* lpart = nullptr;
 };
 
 struct BwdArgs {
@@ -106,6 +113,34 @@ inline SplitPlan plan_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int
   const int64_t used = (Nk + p.C - 1) / p.C;           // non-empty splits
   p.S4 = (int)((used + 3) / 4 * 4);
   return p;
+}
+// Split-KV with as many queries as keys (a prefill whose own grid leaves CUs idle): the
+// general forward kernel with a key split, then the LSE combine.  Default: two splits when
+// fa_fwd's grid would have at most 128 workgroups of 192 rows, else one (measured: at
+// N = 1K-2K the fp32 parts and the combine cost more than further splits save, and above
+// that grid fa_fwd fills the CUs by itself).  One split writes O and LSE directly.
+constexpr int64_t kPrefillSplitMinRows = 128;   // Nq == Nk at least this long takes this route
+struct PrefillSplit {
+  int S, C;   // splits used, keys per split (a multiple of 64)
+};
+inline bool splitkv_is_prefill(int64_t Nq, int64_t Nk) { return Nq == Nk && Nq >= kPrefillSplitMinRows; }
+inline PrefillSplit plan_prefill_split(int64_t B, int64_t Hq, int64_t N, int64_t num_splits) {
+  const int64_t tiles = (N + 63) / 64;
+  int64_t S = num_splits;
+  if (S <= 0) S = B * Hq * ((N + 191) / 192) <= 128 ? 2 : 1;
+  if (S > tiles) S = tiles;
+  if (S < 1) S = 1;
+  const int64_t per = (tiles + S - 1) / S;
+  PrefillSplit p;
+  p.C = (int)(per * 64);
+  p.S = (int)((tiles + per - 1) / per);
+  return p;
+}
+inline size_t prefill_opart_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d, const PrefillSplit& p) {
+  return p.S == 1 ? 0 : (size_t)((B * Hq * N * p.S * d * 4 + 255) / 256 * 256);
+}
+inline size_t prefill_workspace_bytes(int64_t B, int64_t Hq, int64_t N, int64_t d, const PrefillSplit& p) {
+  return p.S == 1 ? 0 : prefill_opart_bytes(B, Hq, N, d, p) + (size_t)((B * Hq * N * p.S * 4 + 255) / 256 * 256);
 }
 inline size_t splitkv_opart_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, const SplitPlan& p) {
   return (size_t)((B * Hq * Nq * (p.S4 / 4) * d * 4 + 255) / 256 * 256);

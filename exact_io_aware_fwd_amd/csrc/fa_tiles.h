@@ -105,10 +105,9 @@ struct TilePair {
 // (batch, kv-head) groups is a multiple of 8, XCD x serves groups x, x+8, ... so
 // their K/V stay in that XCD's L2.  Within an XCD, slots run over query blocks
 // from the last (longest when causal) down.
-__device__ __forceinline__ void map_q_block(int nqb, int B, int Hq, int Hkv, int& b, int& hq, int& iq) {
+__device__ __forceinline__ void map_q_block(int nqb, int B, int Hq, int Hkv, int& b, int& hq, int& iq, int bid) {
   const int G = Hq / Hkv;
   const int ngroups = B * Hkv;
-  const int bid = blockIdx.x;
   int grp, gq, iq_rev;
   if ((ngroups & 7) == 0) {
     const int x = bid & 7, s = bid >> 3;
@@ -127,6 +126,9 @@ __device__ __forceinline__ void map_q_block(int nqb, int B, int Hq, int Hkv, int
   iq = nqb - 1 - iq_rev;
   b = grp / Hkv;
   hq = (grp - b * Hkv) * G + gq;
+}
+__device__ __forceinline__ void map_q_block(int nqb, int B, int Hq, int Hkv, int& b, int& hq, int& iq) {
+  map_q_block(nqb, B, Hq, Hkv, b, hq, iq, (int)blockIdx.x);
 }
 
 }  // namespace fa

@@ -128,6 +128,14 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  *   16-byte aligned; contents on entry are ignored.
  *   B = 0 or Nq = 0: nothing to do, FA_OK.  Nk = 0 with Nq > 0 is invalid (no keys).
  * Same dtype/d rules and status codes as fa_fwd.
+ *
+ * As many queries as keys (Nq == Nk >= 128): the same split applied to a whole
+ * sequence, for calls whose fa_fwd grid would leave compute units idle (one short
+ * sequence, few heads).  Every query block of fa_fwd's forward is computed by
+ * num_splits workgroups, each over a contiguous range of 64-key tiles (default: enough
+ * splits for about 512 workgroups of 192 queries, at most 16), and the parts are merged
+ * by the same log-sum-exp combine; num_splits then counts splits per query block and
+ * the split size is rounded to 64 keys.
  */
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          void* workspace, size_t workspace_bytes,
@@ -138,13 +146,13 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
 /*
  * Bytes of workspace fa_fwd_splitkv needs: per output row and group of four splits
  * (the splits padded to a multiple of 4), the fp32 partial O (d floats) and partial
- * LSE.  0 for invalid sizes.
+ * LSE; with Nq == Nk >= 128, per output row and split.  0 for invalid sizes.
  */
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                                      fa_dtype dtype, int64_t num_splits);
 
 /* The number of key splits fa_fwd_splitkv uses for num_splits = 0 (before padding to
- * a multiple of 4); 0 for invalid sizes. */
+ * a multiple of 4; with Nq == Nk >= 128, splits per query block); 0 for invalid sizes. */
 int64_t fa_fwd_splitkv_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d);
 
 /*

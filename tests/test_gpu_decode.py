@@ -55,6 +55,31 @@ def test_splitkv_split_counts(num_splits):
     check_splitkv(q, k, v, True, 0.0883883, num_splits=num_splits, label="splits")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,N,causal,S", [(1, 8, 2, 128, True, 0), (1, 8, 2, 1000, True, 0),
+                                                 (1, 4, 4, 1024, False, 0), (2, 4, 1, 1100, True, 5),
+                                                 (1, 2, 1, 777, False, 16), (1, 6, 3, 300, True, 10_000)])
+def test_prefill_key_split(dtype, d, B, Hq, Hkv, N, causal, S):
+    """As many queries as keys (>= 128): fa_fwd_splitkv cuts every query block's keys into
+    64-key-aligned splits and merges the parts; ragged N, causal splits past a block's
+    diagonal (empty parts), explicit counts up to one split per tile, GQA and MQA."""
+    q, k, v = _inputs(400 + N + d + S, B, Hq, Hkv, N, N, d, dtype)
+    check_splitkv(q, k, v, causal, float(np.float32(d ** -0.5)), num_splits=S, label=f"prefill N={N}")
+
+
+def test_prefill_key_split_matches_fa_fwd_on_a_small_grid():
+    """The key-split route against fa_fwd on the shape it is for (one sequence of 1024
+    tokens, 32 query heads over 8 K/V heads): both within the oracle's tolerance, and
+    within the bf16 output rounding of each other."""
+    q, k, v = _inputs(450, 1, 32, 8, 1024, 1024, 128, torch.bfloat16)
+    o1, l1 = check_splitkv(q, k, v, True, 0.0883883, label="small grid")
+    o2, l2 = fa.fwd(*to_dev(q, k, v), causal=True, softmax_scale=0.0883883)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o2.float().abs().max().item()
+    assert (l1 - l2).abs().max().item() <= 2e-5
+
+
 def test_splitkv_mqa_and_mha():
     q, k, v = _inputs(310, 1, 16, 1, 3, 777, 128, torch.bfloat16)      # MQA: 48 rows -> two row groups
     check_splitkv(q, k, v, True, 0.0883883, label="mqa")
