@@ -82,8 +82,8 @@ __global__ void __launch_bounds__(256) bwd_rowterm_kernel(const BwdArgs a, long 
     const u32x4 g4 = *(const u32x4*)((const unsigned char*)a.dout + (row * D + part * 8) * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc += E::to_f32((uint16_t)(o4[i] & 0xffff)) * E::to_f32((uint16_t)(g4[i] & 0xffff));
-      acc += E::to_f32((uint16_t)(o4[i] >> 16)) * E::to_f32((uint16_t)(g4[i] >> 16));
+      acc = fmaf(E::to_f32((uint16_t)(o4[i] & 0xffff)), E::to_f32((uint16_t)(g4[i] & 0xffff)), acc);
+      acc = fmaf(E::to_f32((uint16_t)(o4[i] >> 16)), E::to_f32((uint16_t)(g4[i] >> 16)), acc);
     }
   }
 #pragma unroll
@@ -1205,12 +1205,43 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
       qf[s] = *(const u32x4*)(qp + 32 * s);
       df[s] = *(const u32x4*)(gp + 32 * s);
     }
-    const long long t = rowterm_index((long long)b * a.Hq + hq, ((GEN ? a.maxq : N) + 31) / 32, myq);
-    lse2 = a.rowterm[t];
-    negd = a.rowterm[t + 32];
+    if (GEN || !a.rowterm_here) {
+      const long long t = rowterm_index((long long)b * a.Hq + hq, ((GEN ? a.maxq : N) + 31) / 32, myq);
+      lse2 = a.rowterm[t];
+      negd = a.rowterm[t + 32];
+    } else {
+      // the row terms of fa_bwd formed here, for this pass and (written below) the dK/dV
+      // pass: D in the row-term kernel's order (each 8-element part summed in sequence,
+      // then the parts pairwise: the partner half-wave, then s ^ 1, s ^ 2, s ^ 4)
+      const unsigned char* op = (const unsigned char*)a.o + (qhead + myq) * ROWB + 16 * hh;
+      float part[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 o4 = *(const u32x4*)(op + 32 * s), g4 = df[s];
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = fmaf(E::to_f32((uint16_t)(o4[i] & 0xffff)), E::to_f32((uint16_t)(g4[i] & 0xffff)), acc);
+          acc = fmaf(E::to_f32((uint16_t)(o4[i] >> 16)), E::to_f32((uint16_t)(g4[i] >> 16)), acc);
+        }
+        part[s] = half_sum(acc);
+      }
+#pragma unroll
+      for (int w = 1; w < NS; w <<= 1)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          if ((s & w) == 0 && (s & (w - 1)) == 0) part[s] = part[s] + part[s + w];
+      lse2 = a.lse[qhead + myq] * kLog2e;
+      negd = -part[0];
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = df[s] = u32x4{0, 0, 0, 0};
+  }
+  if (!GEN && a.rowterm_here && qw < N && hh == 0) {   // (rows past N of the block: zeros)
+    const long long t = rowterm_index((long long)b * a.Hq + hq, (N + 31) / 32, myq);
+    a.rowterm[t] = lse2;
+    a.rowterm[t + 32] = negd;
   }
   // dP^T of every unit starts from -D (this lane's query), so dP - D comes out of the MFMA
   f32x16 ndv;
@@ -1542,15 +1573,12 @@ static hipError_t launch_dq(const BwdArgs& a, int nq, bool causal, hipStream_t s
 }
 
 template <class Tag, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const long long prows = (long long)a.B * a.Hq * ((a.N + 31) / 32) * 32;   // padded rows
+static hipError_t launch_bwd_t(const BwdArgs& a0, hipStream_t stream) {
+  const long long prows = (long long)a0.B * a0.Hq * ((a0.N + 31) / 32) * 32;   // padded rows
   if (prows <= 0) return hipSuccess;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_rowterm_kernel<Tag, D>), dim3((unsigned)((prows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, a, prows);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
+  BwdArgs a = a0;
+  a.rowterm_here = 1;   // the dQ pass forms and writes the row terms (no row-term kernel)
+  hipError_t err = launch_dq<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
   if (err != hipSuccess) return err;
   if (a.kblock == 256) {   // 64 keys a wave
     const long long nrec256 = (a.N + 255) / 256 * a.B * a.Hkv;

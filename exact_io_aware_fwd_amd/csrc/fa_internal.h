@@ -72,6 +72,7 @@ struct BwdArgs {
   // key block, record = (batch * Hkv + K/V head) * key blocks + key block)
   int ksplit = 1;
   int kblock = 128;   // fa_bwd: keys per dK/dV record, 256 (64 keys a wave) or 128 (32)
+  int rowterm_here = 0;   // fa_bwd: the dQ pass forms the row terms and writes them
 };
 
 // Split-KV forward (decoding): queries [B, Hq, Nq, d] against keys/values [B, Hkv, Nk, d].
