@@ -506,14 +506,15 @@ def bench_masks(args):
 
 def _dkdv_kernels(B, Hq, Hkv, N, causal):
     """The dK/dV launches fa_bwd makes for these sizes (its choice, restated for the label):
-    records of 256 keys (64 a wave) or 128, split into chunks (and a reduction) when few."""
+    records of 256 keys (64 a wave) or 128, split into chunks (and a reduction) when few;
+    with the dQ pass (which also forms the row terms) the launch count of the backward."""
     steps, target = (Hq // Hkv) * -(-N // 32), 512 if causal else 256
     chunks = lambda r, m: max(min(target // r, 16, steps // m), 1)
     r256, r128 = B * Hkv * -(-N // 256), B * Hkv * -(-N // 128)
     name, k = (("bwd_dkdv64_kernel", chunks(r256, 256))
                if r256 >= target or r256 * chunks(r256, 256) >= r128 * chunks(r128, 32)
                else ("bwd_dkdv_kernel", chunks(r128, 32)))
-    return (name + " + bwd_reduce_kernel", 4) if k > 1 else (name, 3)
+    return (name + " + bwd_reduce_kernel", 3) if k > 1 else (name, 2)
 
 
 def bench_sweep(args):
@@ -672,7 +673,7 @@ def main():
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak
     if not args.fwd_only:
         dkdv, nl = _dkdv_kernels(w.B, w.Hq, w.Hkv, w.N, causal)
-        passes["bwd"] = {"kernel": "bwd_rowterm_kernel + bwd_dq_kernel + " + dkdv, "launches": nl,
+        passes["bwd"] = {"kernel": "bwd_dq_kernel + " + dkdv, "launches": nl,
                          "ms": bwd_ms, "median_ms": med(bwd_t), "min_ms": bwd_t[0],
                          "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
                          "tflops_median": f_bwd / (med(bwd_t) * 1e-3) / 1e12}
