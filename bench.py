@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--fwd-only", action="store_true", help="time only the forward pass (profiling)")
     p.add_argument("--cpu-heads", type=int, default=12, help="query heads in the CPU-baseline sample")
     p.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy and exit")
+    p.add_argument("--gemm-calibration", action="store_true",
+                   help="time a plain bf16 8192^3 GEMM (vendor BLAS) and exit")
     p.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 CSV output under DIR and exit")
     p.add_argument("--pmc", action="store_true", help="with --summarize: counter CSVs instead of kernel trace")
     p.add_argument("--record-traffic", nargs=3, metavar=("KERNEL_DIR", "COPY_DIR", "KERNEL_SUBSTR"),
@@ -116,6 +118,33 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 5}))
+
+
+def gemm_calibration():
+    """A plain bf16 GEMM through torch (the vendor BLAS), 8192 x 8192 x 8192, timed with HIP
+    events after 1 s of warm-up: the matrix-core rate a library product reaches on this part
+    under the same power and clock limits as the attention kernels."""
+    import torch
+    from exact_io_aware_fwd_amd import metrics
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        c = a @ b
+        torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2 * n ** 3 / ms / 1e9
+    print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}", "ms": ms, "tflops": tf, "frac_of_peak": tf / metrics.MFMA_BF16_TFLOPS}))
+    del c
 
 
 def _read_csv(pattern):
@@ -519,7 +548,8 @@ def _dkdv_kernels(B, Hq, Hkv, N, causal):
 
 def bench_sweep(args):
     """Forward and backward TFLOP/s (algorithmic FLOPs / time with HIP events on the launch
-    stream, best of three rounds of 10 calls each) over d in {128, 64}, (B, Hq, Hkv) in
+    stream, best of three rounds of 10 calls each, the rounds of the three calls interleaved so that
+    each sees the same clocks) over d in {128, 64}, (B, Hq, Hkv) in
     {(1, 16, 16), (1, 32, 8), (2, 32, 8), (4, 32, 8)}, N from 1K to 16K (at most 1M query
     rows), causal or not; seeded N(0, 1) bf16 inputs, and fp16 ones at d = 128, N >= 4K.
     The forward is timed twice: fa_fwd, and fa_fwd_splitkv with as many queries as keys
@@ -533,18 +563,20 @@ def bench_sweep(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    def best_ms(fn, reps=10, rounds=3):
-        fn()
+    def best_ms(fns, reps=10, rounds=3):
+        for fn in fns:
+            fn()
         torch.cuda.synchronize()
-        best = float("inf")
+        best = [float("inf")] * len(fns)
         for _ in range(rounds):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) / reps)
+            for i, fn in enumerate(fns):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                best[i] = min(best[i], e0.elapsed_time(e1) / reps)
         return best
 
     warm_until = time.perf_counter() + 0.3    # let the clocks ramp before the first shape
@@ -572,9 +604,12 @@ def bench_sweep(args):
                         while time.perf_counter() < warm_until:
                             fwd()
                             torch.cuda.synchronize()
-                        tf = best_ms(fwd)
-                        ts = best_ms(lambda: fa.fwd_splitkv(q, k, v, causal=causal, workspace=wss, out=o, lse=lse))
-                        tb = best_ms(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws))
+                        # the backward reads the forward's O and LSE: fa_fwd and the key-split
+                        # route write the same values (within rounding) into them
+                        tf, ts, tb = best_ms([
+                            fwd,
+                            lambda: fa.fwd_splitkv(q, k, v, causal=causal, workspace=wss, out=o, lse=lse),
+                            lambda: fa.bwd(q, k, v, o, lse, do, causal=causal, workspace=ws)])
                         ff = metrics.fwd_flops(B, Hq, N, d, causal)
                         fb = metrics.bwd_flops(B, Hq, N, d, causal)
                         name = {torch.bfloat16: "bf16", torch.float16: "fp16"}[dt]
@@ -591,6 +626,9 @@ def main():
         return
     if args.record_traffic:
         record_traffic(*args.record_traffic)
+        return
+    if args.gemm_calibration:
+        gemm_calibration()
         return
     if args.copy_calibration:
         copy_calibration()

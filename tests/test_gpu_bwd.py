@@ -41,6 +41,8 @@ def check_bwd(q, k, v, do, causal, scale, label="", vs_baseline=False):
             if np.linalg.norm(r.ravel()) > floor:
                 bound[n] = max(GRAD_TOL, 2 * float(np.linalg.norm((b - r).ravel()) / np.linalg.norm(r.ravel())))
     for n, e in errs.items():
+        if bound[n] > GRAD_TOL:   # the baseline-relative bound was needed: say by how much
+            say(f"    {n}: rel-L2 {e:.3e}, bound {bound[n]:.3e} (baseline-relative; fixed bound {GRAD_TOL:.0e})")
         assert np.isfinite(e) and e <= bound[n], f"{n} rel-L2 {e:.3e} > {bound[n]:.3e} ({label})"
     return errs
 
@@ -51,7 +53,9 @@ def check_bwd(q, k, v, do, causal, scale, label="", vs_baseline=False):
 def test_small_and_ragged(N, d, dtype):
     q, k, v, do = workloads.random_case(30 * N + d, 1, 4, 2, N, d, dtype, with_do=True)
     for causal in (False, True):
-        check_bwd(q, k, v, do, causal, 1 / math.sqrt(d), label=f"N={N} d={d}", vs_baseline=True)
+        errs = check_bwd(q, k, v, do, causal, 1 / math.sqrt(d), label=f"N={N} d={d}", vs_baseline=True)
+        if N >= 32:   # the fixed bound holds from 32 keys on; the relaxed one is for a handful of keys
+            assert all(e <= GRAD_TOL for e in errs.values()), (N, d, dtype, causal, errs)
 
 
 @pytest.mark.parametrize("case", [
