@@ -23,6 +23,7 @@ import oracle.masks as om
 import workloads
 from tests.gpu_util import GRAD_TOL, rel_l2, say, to_dev
 import exact_io_aware_fwd_amd as fa
+from tests.bwd_plan import dense_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -229,22 +230,32 @@ def test_bwd_masked_all_tiles_listed_equals_no_lists():
             assert torch.equal(a, b) and torch.equal(b, c)
 
 
-@pytest.mark.parametrize("B,causal", [(2, False), (4, False), (4, True)])
+@pytest.mark.parametrize("B,causal", [(2, False), (4, False), (4, True), (2, True)])
 def test_bwd_masked_equals_bwd_bitwise(B, causal):
     """Without a mask the general mode equals fa_bwd bit for bit where fa_bwd does not split
     its dK/dV records into chunks with fp32 partials (a split sums in another order): from
-    256 blocks of 256 keys on (512 when causal), where it runs 64 keys a wave."""
+    256 blocks of 256 keys on (512 when causal), where it runs 64 keys a wave.  Where it
+    splits (B = 2 causal: 256 records of 256 keys, two chunks each) dQ is still equal bit for
+    bit and dK, dV differ only by the order of the fp32 partial sums before rounding."""
     Hq, Hkv, N = 8, 4, 8192
     q, k, v, do = to_dev(_rand(9660, (B, Hq, N, 128)), _rand(9661, (B, Hkv, N, 128)), _rand(9662, (B, Hkv, N, 128)),
                          _rand(9663, (B, Hq, N, 128)))
-    say(f"[bwd masked] equals fa_bwd bit for bit, B={B} causal={causal}")
+    split = dense_plan(B, Hq, Hkv, N, causal)[1] > 1
+    assert split == (B == 2 and causal)
+    say(f"[bwd masked] equals fa_bwd {'within rounding (split dK/dV)' if split else 'bit for bit'}, "
+        f"B={B} causal={causal}")
     for window in ((-1, 0),) if causal else ((-1, -1),):
         o, lse = fa.fwd(q, k, v, causal=causal)
         g1 = fa.bwd(q, k, v, o, lse, do, causal=causal)
         g2 = fa.bwd_masked(q, k, v, o, lse, do, window)
         torch.cuda.synchronize()
-        for a, b in zip(g1, g2):
-            assert torch.equal(a, b)
+        for i, (a, b) in enumerate(zip(g1, g2)):
+            if split and i > 0:   # fp32 sums in another order, then one rounding to bf16
+                diff = (a.float() - b.float()).abs()
+                assert diff.max().item() <= 2.0 ** -6 * b.float().abs().max().item()
+                assert (diff.norm() / b.float().norm()).item() <= 1e-3
+            else:
+                assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("d,dt,window", [(128, torch.bfloat16, (200, 0)), (64, torch.float16, (100, 40)),
