@@ -631,7 +631,7 @@ fwd_unit_kernel(const FwdArgs a) {
     }
     // P from the reference as it stands, with no row max: any reference gives the same
     // normalised result, it only has to keep P from overflowing.  If this lane's
-    // probabilities sum past 2^TAU (so some P may exceed 2^TAU, or the lane has no
+    // probabilities sum past TAU_SUM = 2^8 (so some P may exceed 2^8, or the lane has no
     // reference yet, whose sentinel -FLT_MAX makes every visible P infinite), the wave
     // takes the slow path: the row max of the unit, the reference raised to it, O and
     // the row sum rescaled, P formed again.  Masked scores (-inf) give P = 0 either way.
