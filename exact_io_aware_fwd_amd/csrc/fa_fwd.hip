@@ -488,9 +488,15 @@ fwd_unit_kernel(const FwdArgs a) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;
-  constexpr int PK = ROWB + 16;
-  constexpr int PV = ROWB + 64;
-  using Tiles = TilePair<ROWB, PK, PV, NW>;
+  // K and V tiles free of bank conflicts for the row reads of K and the transposing reads
+  // of V: at d = 64 unpadded with their 16-byte chunks XOR-swizzled (fa_tiles.h), 20 %
+  // fewer tile loads (up to 2.4 % faster); at d = 128 padded (K row+16 B, V row+64 B), since
+  // the swizzled addresses take ~12 more registers a wave there and cost 1.5-2.7 %
+  constexpr bool SWZ = D == 64;
+  constexpr int PK = SWZ ? ROWB : ROWB + 16;
+  constexpr int PV = SWZ ? ROWB : ROWB + 64;
+  using Tiles = TilePair<ROWB, PK, PV, NW, SWZ, SWZ>;
+  using SO = SwzOffsets<ROWB>;
   constexpr int KBYTES = Tiles::ABYTES;
   constexpr int SLOT = Tiles::SLOT;
   constexpr int IPW = Tiles::IPW;
@@ -587,17 +593,23 @@ fwd_unit_kernel(const FwdArgs a) {
     uhi = qw >= N ? -1 : CAUSAL ? min(qw + 31, N - 1) : N - 1;
     whi = CAUSAL ? min(qw, N - 1) : N - 1;
   }
-  // K rows (A operand of S^T) and V read transposed (A operand of O^T), as in fwd_kernel
+  // K rows 32h + r32, chunk 2st + hh (A operand of S^T); V read transposed, rows
+  // 32hv + 16h + 8u + R (A operand of O^T): the operands of fwd_kernel, from swizzled rows
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  const int ka = r32 * PK + 16 * hh;
-  const int va = KBYTES + (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  const int ka = SWZ ? SO::rows_a0(lane) : r32 * PK + 16 * hh;
+  const int va = KBYTES + (SWZ ? SO::tr_lane(lane)
+                               : (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
   auto kread = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
-    return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
+    if constexpr (SWZ) return *(const u32x4*)(sl + h * 32 * PK + (ka ^ (st << 5)));
+    else return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
   };
   auto vread = [&](const unsigned char* sl, int hv, int h, int e) __attribute__((always_inline)) {
-    const unsigned char* p = sl + hv * 32 * PV + va;
-    return cat(lds_read_tr(p + 16 * h * PV + 64 * e), lds_read_tr(p + (16 * h + 8) * PV + 64 * e));
+    const unsigned char* p = sl + (32 * hv + 16 * h) * PV;
+    if constexpr (SWZ)
+      return cat(lds_read_tr(p + (va ^ SO::tr_inst(e, 0))), lds_read_tr(p + 8 * PV + (va ^ SO::tr_inst(e, 1))));
+    else
+      return cat(lds_read_tr(p + va + 64 * e), lds_read_tr(p + 8 * PV + va + 64 * e));
   };
   const float c2 = a.scale_log2;
   float mr = -FLT_MAX, l_run = 0.f;   // reference (log2 units); -FLT_MAX: none yet

@@ -45,14 +45,14 @@ struct SwzOffsets {
 };
 
 // A pair of 64-row tiles (tensor A then tensor B) in one LDS slot, rows padded to
-// pitches PA and PB bytes, or, with SWZ_A, tensor A unpadded (PA == ROWB) with its
-// chunks swizzled as above.  With the 64 four-byte banks of the CDNA4 LDS:
+// pitches PA and PB bytes, or, with SWZ_A (SWZ_B), tensor A (B) unpadded with its chunks
+// swizzled as above.  With the 64 four-byte banks of the CDNA4 LDS:
 //   pitch row+16 B: 16 lanes reading 16 bytes from 16 consecutive rows hit distinct banks;
 //   pitch row+64 B: 32 lanes reading 8 bytes from 4 consecutive rows (ds_read_b64_tr_b16)
 //                   hit distinct banks.
 // Both were measured free of bank conflicts.  The slot is filled by wave-wide
 // 16-byte-per-lane loads: load n (n = wave + NW*i) covers slot bytes [1024n, 1024n+1024).
-template <int ROWB, int PA, int PB, int NW, bool SWZ_A = false>
+template <int ROWB, int PA, int PB, int NW, bool SWZ_A = false, bool SWZ_B = false>
 struct TilePair {
   static constexpr int ABYTES = 64 * PA;
   static constexpr int BBYTES = 64 * PB;
@@ -65,6 +65,7 @@ struct TilePair {
   // Byte of the tile's rows that this lane's 16 bytes of load i come from.  Lanes
   // landing on row padding re-fetch byte 0 (any valid address will do).
   static_assert(!SWZ_A || PA == ROWB, "a swizzled tile is unpadded");
+  static_assert(!SWZ_B || PB == ROWB, "a swizzled tile is unpadded");
   static __device__ __forceinline__ void offsets(int wave, int lane, int* doff) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -72,7 +73,7 @@ struct TilePair {
       const int P = n < AI ? PA : PB;
       const int o = (n < AI ? n : n - AI) * 1024 + lane * 16;
       const int row = o / P, col = o - (o / P) * P;
-      if (SWZ_A && n < AI)
+      if ((SWZ_A && n < AI) || (SWZ_B && n >= AI))
         doff[i] = row * ROWB + (((col >> 4) ^ swz<ROWB / 16>(row)) << 4);
       else
         doff[i] = col < ROWB ? row * ROWB + col : 0;
