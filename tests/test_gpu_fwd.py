@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads
 import exact_io_aware_fwd_amd as fa
-from tests.gpu_util import O_TOL, LSE_TOL, check_fwd, o_err, say, to_dev
+from tests.gpu_util import O_TOL, LSE_TOL, check_fwd, lse_err, o_err, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +137,28 @@ def test_forward_is_bitwise_deterministic():
     o2, l2 = fa.fwd(q, k, v, causal=True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     del w
+
+
+@pytest.mark.parametrize("d,dt,N", [(128, torch.bfloat16, 1000), (64, torch.float16, 777), (128, torch.float16, 4100)])
+def test_forward_writes_every_output_element(d, dt, N):
+    """O and LSE prefilled with NaN: after fa_fwd every element is finite and matches the
+    oracle on sampled rows (each lane's 16-byte pieces of O, swapped between the two
+    half-waves, must land on the row's every column)."""
+    B, Hq, Hkv = 2, 4, 2
+    q, k, v = workloads.random_case(700 + N + d, B, Hq, Hkv, N, d, dt)
+    qd, kd, vd = to_dev(q, k, v)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    for causal in (False, True):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        fa.fwd(qd, kd, vd, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        rows = np.array([0, 1, 31, 32, 63, 200, N // 2, N - 2, N - 1])
+        O_ref, L_ref = oracle.attention_fwd(q, k, v, causal, 1 / math.sqrt(d), rows=rows)
+        assert o_err(o[:, :, rows].cpu(), O_ref) <= O_TOL[dt]
+        assert lse_err(lse[:, :, rows].cpu(), L_ref) <= LSE_TOL
 
 
 def test_forward_allocates_nothing():
