@@ -736,21 +736,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T, rounded to the input dtype
-  if (mykey < Lk) {
-    unsigned char* dKg = (unsigned char*)a.dk + (kvhead + mykey) * ROWB;
-    unsigned char* dVg = (unsigned char*)a.dv + (kvhead + mykey) * ROWB;
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * e + 8 * g4 + 4 * hh;
-        const u32x2 wk = {E::pack(dk[e][4 * g4 + 0] * a.scale, dk[e][4 * g4 + 1] * a.scale),
-                          E::pack(dk[e][4 * g4 + 2] * a.scale, dk[e][4 * g4 + 3] * a.scale)};
-        const u32x2 wv = {E::pack(dv[e][4 * g4 + 0], dv[e][4 * g4 + 1]),
-                          E::pack(dv[e][4 * g4 + 2], dv[e][4 * g4 + 3])};
-        *(u32x2*)(dKg + d0 * 2) = wk;
-        *(u32x2*)(dVg + d0 * 2) = wv;
-      }
+  if (mykey < Lk) {   // (both lanes of a key take this together)
+    store_row16<E>((unsigned char*)a.dk + (kvhead + mykey) * ROWB, dk, a.scale, hh);
+    store_row16<E>((unsigned char*)a.dv + (kvhead + mykey) * ROWB, dv, 1.f, hh);
   }
 }
 
@@ -1029,19 +1017,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv64_kernel(const BwdArgs a) {
   acc_drain(dv1);
   auto store = [&](const f32x16 (&dk)[NE], const f32x16 (&dv)[NE], int key) __attribute__((always_inline)) {
     if (key >= N) return;
-    unsigned char* dKg = (unsigned char*)a.dk + (kvhead + key) * ROWB;
-    unsigned char* dVg = (unsigned char*)a.dv + (kvhead + key) * ROWB;
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * e + 8 * g4 + 4 * hh;
-        const u32x2 wk = {E::pack(dk[e][4 * g4 + 0] * a.scale, dk[e][4 * g4 + 1] * a.scale),
-                          E::pack(dk[e][4 * g4 + 2] * a.scale, dk[e][4 * g4 + 3] * a.scale)};
-        const u32x2 wv = {E::pack(dv[e][4 * g4 + 0], dv[e][4 * g4 + 1]), E::pack(dv[e][4 * g4 + 2], dv[e][4 * g4 + 3])};
-        *(u32x2*)(dKg + d0 * 2) = wk;
-        *(u32x2*)(dVg + d0 * 2) = wv;
-      }
+    store_row16<E>((unsigned char*)a.dk + (kvhead + key) * ROWB, dk, a.scale, hh);
+    store_row16<E>((unsigned char*)a.dv + (kvhead + key) * ROWB, dv, 1.f, hh);
   };
   if constexpr (SPLIT) {
     if (nsplit > 1) {   // fp32 partial dK^T (unscaled) then dV^T of the 256 keys, as [key][d]
@@ -1529,17 +1506,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
 
   // dQ = scale * (dQ^T)^T, rounded to the input dtype
   if (myq < Lq) {
-    unsigned char* Og = (unsigned char*)a.dq + (qhead + myq) * ROWB;
-    const float sc = a.scale;
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * e + 8 * g + 4 * hh;
-        const u32x2 w = {E::pack(acc[e][4 * g + 0] * sc, acc[e][4 * g + 1] * sc),
-                         E::pack(acc[e][4 * g + 2] * sc, acc[e][4 * g + 3] * sc)};
-        *(u32x2*)(Og + d0 * 2) = w;
-      }
+    store_row16<E>((unsigned char*)a.dq + (qhead + myq) * ROWB, acc, a.scale, hh);
   }
 }
 

@@ -149,6 +149,38 @@ static __device__ __forceinline__ float half_sum(float x) {
 
 static __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Write one row of a transposed accumulator (x^T in NE 32x32 MFMA C tiles: this lane holds
+// elements 32e + 8g + 4hh + 0..3 of its row, g = 0..3), times `mul`, rounded to the element
+// type, 16 bytes a lane.  Of each pair of 8-element chunks 32e + 16m and 32e + 16m + 8, the
+// lane with hh = 0 writes the first (its own 4 elements, then its partner's) and the lane
+// with hh = 1 the second; the partners (lanes l and l + 32, the same row) swap one 8-byte
+// piece with permlane32_swap.  Both partners must take this call together (they share the
+// row, so a row bound keeps them in step).
+template <class E, int NE>
+static __device__ __forceinline__ void store_row16(unsigned char* row, const f32x16 (&x)[NE], float mul, int hh) {
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t w[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int g = 2 * m + t;
+        w[t][0] = E::pack(x[e][4 * g + 0] * mul, x[e][4 * g + 1] * mul);
+        w[t][1] = E::pack(x[e][4 * g + 2] * mul, x[e][4 * g + 3] * mul);
+      }
+      uint32_t y[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t send = hh ? w[0][j] : w[1][j];
+        const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+        y[j] = hh ? r[0] : r[1];
+      }
+      const u32x4 out = hh ? u32x4{y[0], y[1], w[1][0], w[1][1]} : u32x4{w[0][0], w[0][1], y[0], y[1]};
+      *(u32x4*)(row + (32 * e + 16 * m + 8 * hh) * 2) = out;
+    }
+}
+
 // Smallest p in [0, n) with list[p] >= t (n if none); list ascending (block lists).
 static __device__ __forceinline__ int lower_bound_tiles(const int* list, int n, int t) {
   int lo = 0, hi = n;

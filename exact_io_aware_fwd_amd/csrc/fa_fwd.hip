@@ -454,16 +454,7 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
   const float l_tot = half_sum(l_run);
   if (myq < Lq) {
     const float inv = (GEN && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
-    unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * e + 8 * g + 4 * hh;
-        const u32x2 w = {E::pack(o[e][4 * g + 0] * inv, o[e][4 * g + 1] * inv),
-                         E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
-        *(u32x2*)(Og + d0 * 2) = w;
-      }
+    store_row16<E>((unsigned char*)a.o + (qhead + myq) * ROWB, o, inv, hh);
     if (hh == 0) a.lse[qhead + myq] = (GEN && !(l_tot > 0.f)) ? -INFINITY : (mr + log2f(l_tot)) * kLn2;
   }
 }
@@ -747,31 +738,8 @@ fwd_unit_kernel(const FwdArgs a) {
   }
   if (myq < Lq) {
     const float inv = (GEN && !(l_tot > 0.f)) ? 0.f : 1.f / l_tot;
-    unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * ROWB;
-    // 16 bytes a lane: of each pair of 8-element chunks 16m, 16m + 8 of block e, the lane
-    // with hh = 0 writes the first (its own 4 elements, then its partner's) and the lane
-    // with hh = 1 the second; the partners (lanes l, l + 32) swap one 8-byte piece
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint32_t w[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int g = 2 * m + t;
-          w[t][0] = E::pack(o[e][4 * g + 0] * inv, o[e][4 * g + 1] * inv);
-          w[t][1] = E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv);
-        }
-        uint32_t y[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t x = hh ? w[0][j] : w[1][j];
-          const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-          y[j] = hh ? r[0] : r[1];
-        }
-        const u32x4 out = hh ? u32x4{y[0], y[1], w[1][0], w[1][1]} : u32x4{w[0][0], w[0][1], y[0], y[1]};
-        *(u32x4*)(Og + (32 * e + 16 * m + 8 * hh) * 2) = out;
-      }
+    // 16 bytes a lane (store_row16: the two lanes of the row swap an 8-byte piece)
+    store_row16<E>((unsigned char*)a.o + (qhead + myq) * ROWB, o, inv, hh);
     if (hh == 0) a.lse[qhead + myq] = (GEN && !(l_tot > 0.f)) ? -INFINITY : (mr + log2f(l_tot)) * kLn2;
   }
 }

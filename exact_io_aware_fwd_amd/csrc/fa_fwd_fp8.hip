@@ -388,16 +388,7 @@ __global__ void __launch_bounds__(512) fwd_fp8_kernel(const Fp8FwdArgs a) {
   const float l_tot = half_sum(l_run);
   if (myq < N) {
     const float inv = 1.f / l_tot;
-    unsigned char* Og = (unsigned char*)a.o + (qhead + myq) * (size_t)(2 * D);
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * e + 8 * g + 4 * hh;
-        const u32x2 w = {E::pack(o[e][4 * g + 0] * inv, o[e][4 * g + 1] * inv),
-                         E::pack(o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv)};
-        *(u32x2*)(Og + d0 * 2) = w;
-      }
+    store_row16<E>((unsigned char*)a.o + (qhead + myq) * (size_t)(2 * D), o, inv, hh);
     if (hh == 0) a.lse[qhead + myq] = (mr + log2f(l_tot)) * kLn2;
   }
 }
