@@ -533,6 +533,14 @@ def bench_masks(args):
     print(json.dumps(rec), flush=True)
 
 
+def _fwd_kernel(B, Hq, N, d, causal):
+    """The forward kernel fa_fwd launches for these sizes (its choice, restated for the
+    label): 64-query waves at d = 128 once B * Hq * ceil(N / 512) reaches 512 (causal) or
+    256, else 32-query waves."""
+    return ("fwd_unit2_kernel" if d == 128 and B * Hq * -(-N // 512) >= (512 if causal else 256)
+            else "fwd_unit_kernel")
+
+
 def _dkdv_kernels(B, Hq, Hkv, N, causal):
     """The dK/dV launches fa_bwd makes for these sizes (its choice, restated for the label):
     records of 256 keys (64 a wave) or 128, split into chunks (and a reduction) when few;
@@ -705,7 +713,8 @@ def main():
 
     # per pass: mean (the roofline figure), median and min of the per-step event times;
     # tflops and frac from the mean, tflops_median from the median
-    passes = {"fwd": {"kernel": "fwd_unit_kernel", "launches": 1, "ms": fwd_ms, "median_ms": med(fwd_t),
+    passes = {"fwd": {"kernel": _fwd_kernel(w.B, w.Hq, w.N, w.d, causal), "launches": 1, "ms": fwd_ms,
+                      "median_ms": med(fwd_t),
                       "min_ms": fwd_t[0], "tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
                       "tflops_median": f_fwd / (med(fwd_t) * 1e-3) / 1e12}}
     passes["fwd"]["frac"] = passes["fwd"]["tflops"] / peak

@@ -12,12 +12,17 @@
 // tile follows the section "FlashAttention-3" (matmul/softmax interleaving),
 // realised here inside each wave's instruction stream.
 //
-// gfx950 design.  Two kernels share tiles, layouts and the epilogue:
-//  * fwd_unit_kernel (fa_fwd): NW waves x 32 query rows, each wave taking one 32-key
-//    unit at a time while the other waves on its SIMD overlap its softmax with their
-//    products: at d = 128 12 waves (one workgroup per CU, three waves per SIMD), or 6
-//    (two workgroups per CU) when the 384-row grid would leave CUs idle; at d = 64 8
-//    waves, two workgroups per CU (four waves per SIMD).
+// gfx950 design.  Three kernels share tiles, layouts and the epilogue:
+//  * fwd_unit2_kernel (fa_fwd, d = 128, large grids): 8 waves x 64 query rows, each wave
+//    two 32-row halves that share every K and V operand read (half the LDS reads per
+//    product of the 32-row waves, and 512 rows served by each K/V tile loaded), two
+//    waves per SIMD; per half the same steps, and bits, as fwd_unit_kernel.
+//  * fwd_unit_kernel (fa_fwd otherwise, and the mask family without block lists): NW
+//    waves x 32 query rows, each wave taking one 32-key unit at a time while the other
+//    waves on its SIMD overlap its softmax with their products: at d = 128 12 waves (one
+//    workgroup per CU, three waves per SIMD), or 6 (two workgroups per CU) when the
+//    384-row grid would leave CUs idle; at d = 64 8 waves, two workgroups per CU (four
+//    waves per SIMD).
 //  * fwd_kernel (the mask family, fa_fwd_masked): 8 waves x 32 rows (256-row blocks,
 //    the granularity of the block lists), two waves per SIMD, with a software
 //    pipeline per wave: the products S_{u+1} = K_{u+1} Q^T are issued while the
@@ -745,6 +750,251 @@ fwd_unit_kernel(const FwdArgs a) {
 }
 
 
+// The dense forward with 64 queries a wave: two 32-query halves share every K and V
+// operand read (half the LDS read instructions of fwd_unit_kernel per product) and the
+// workgroup of NW waves covers 64 NW rows, so each K/V tile loaded serves more rows.
+// The registers of two halves (O^T and Q of 64 rows, 192 of the 256 a wave has at two
+// waves per SIMD) leave no room to keep the scores past the exponentials, so the rare
+// slow path forms them again from the tile still in LDS.  Per half the steps are those
+// of fwd_unit_kernel (stale reference, slow path past TAU_SUM, the same products in the
+// same order; a unit that only the second half sees adds exact zeros to the first), so
+// the two kernels agree bit for bit.
+template <class Tag, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+fwd_unit2_kernel(const FwdArgs a) {
+  using E = Elt<Tag>;
+  constexpr int BR = 64 * NW;
+  constexpr int BC = 64;
+  constexpr int ROWB = D * 2;
+  constexpr bool SWZ = D == 64;
+  constexpr int PK = SWZ ? ROWB : ROWB + 16;
+  constexpr int PV = SWZ ? ROWB : ROWB + 64;
+  using Tiles = TilePair<ROWB, PK, PV, NW, SWZ, SWZ>;
+  using SO = SwzOffsets<ROWB>;
+  constexpr int KBYTES = Tiles::ABYTES;
+  constexpr int SLOT = Tiles::SLOT;
+  constexpr int IPW = Tiles::IPW;
+  constexpr int NE = D / 32;
+  constexpr int NS = D / 16;
+  constexpr float TAU_SUM = 256.f;   // bound on a lane's sum of P over a unit (2^8)
+  constexpr int NSL = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned char slot2[SLOT];
+  // Q operands of the second half for steps QP .. NS-1 parked in LDS (16 bytes a lane,
+  // each lane reading back only what it wrote): 4 (NS - QP) registers fewer a wave, which
+  // with the scheduling barriers below keeps the kernel within 256 registers unspilled
+  constexpr int QP = NS - 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char qpark[NW * (NS - QP) * 1024];
+  auto slot = [&](int i) __attribute__((always_inline)) -> unsigned char* {
+    return i == 0 ? slot0 : i == 1 ? slot1 : slot2;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5, r32 = lane & 31;
+  const int N = a.N;
+  int b, hq, iq;
+  map_q_block((N + BR - 1) / BR, a.B, a.Hq, a.Hkv, b, hq, iq);
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const size_t qhead = (size_t)(b * a.Hq + hq) * (size_t)N;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * (size_t)N;
+  const unsigned char* Qg = (const unsigned char*)a.q + qhead * ROWB;
+  const unsigned char* Kg = (const unsigned char*)a.k + kvhead * ROWB;
+  const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
+  const int q0 = iq * BR;
+  const int qw = q0 + wave * 64;   // this wave's rows qw .. qw + 63, half f = rows qw + 32 f ..
+  int myq[2];
+  u32x4 qf[2][NS];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    myq[f] = qw + 32 * f + r32;
+    if (myq[f] < N) {
+      const unsigned char* qp = Qg + (size_t)myq[f] * ROWB + 16 * hh;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[f][s] = *(const u32x4*)(qp + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[f][s] = u32x4{0, 0, 0, 0};
+    }
+  }
+  unsigned char* const qpl = qpark + (wave * (NS - QP) * 64 + lane) * 16;
+#pragma unroll
+  for (int st = QP; st < NS; ++st) *(u32x4*)(qpl + (st - QP) * 1024) = qf[1][st];
+  auto qop = [&](int f, int st) __attribute__((always_inline)) -> u32x4 {
+    if (f == 1 && st >= QP) return *(const u32x4*)(qpl + (st - QP) * 1024);
+    return qf[f][st];
+  };
+  const int nkv = (N + BC - 1) / BC;
+  const int ntile = CAUSAL ? min(nkv, (min(q0 + BR, N) - 1) / BC + 1) : nkv;
+  // keys some query of the wave sees: [0, uhi]; keys every query of half f sees: [0, whi[f]]
+  const int uhi = qw >= N ? -1 : CAUSAL ? min(qw + 63, N - 1) : N - 1;
+  int whi[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) whi[f] = CAUSAL ? min(qw + 32 * f, N - 1) : N - 1;
+  int doff[IPW];
+  Tiles::offsets(wave, lane, doff);
+  const int ka = SWZ ? SO::rows_a0(lane) : r32 * PK + 16 * hh;
+  const int va = KBYTES + (SWZ ? SO::tr_lane(lane)
+                               : (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+  auto kread = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
+    if constexpr (SWZ) return *(const u32x4*)(sl + h * 32 * PK + (ka ^ (st << 5)));
+    else return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
+  };
+  auto vread = [&](const unsigned char* sl, int hv, int h, int e) __attribute__((always_inline)) {
+    const unsigned char* p = sl + (32 * hv + 16 * h) * PV;
+    if constexpr (SWZ)
+      return cat(lds_read_tr(p + (va ^ SO::tr_inst(e, 0))), lds_read_tr(p + 8 * PV + (va ^ SO::tr_inst(e, 1))));
+    else
+      return cat(lds_read_tr(p + va + 64 * e), lds_read_tr(p + 8 * PV + va + 64 * e));
+  };
+  const float c2 = a.scale_log2;
+  float mr[2] = {-FLT_MAX, -FLT_MAX}, l_run[2] = {0.f, 0.f};
+  f32x16 o[2][NE];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[f][e][v] = 0.f;
+  // S^T of half f for the keys of unit k0 (half h of slot sl), masked: -inf past the row's
+  // position (causal) or past the end
+  auto mask = [&](f32x16& x, int f, int k0) __attribute__((always_inline)) {
+    if (!(k0 + 31 <= whi[f])) {
+      int lim = N - k0 - 4 * hh;
+      if (CAUSAL) lim = min(lim, myq[f] - k0 - 4 * hh + 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + (v & 3) >= lim) x[v] = -INFINITY;
+    }
+  };
+  auto rowsum = [&](const f32x16& p) __attribute__((always_inline)) {
+    float t[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) t[v] = p[2 * v] + p[2 * v + 1];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t[v] = t[2 * v] + t[2 * v + 1];
+    return (t[0] + t[1]) + (t[2] + t[3]);
+  };
+  // unit u = keys 32u .. 32u+31, half h of the tile in slot sl
+  auto unit = [&](int u, const unsigned char* sl, int h) __attribute__((always_inline)) {
+    const int k0 = u * 32;
+    if (k0 > uhi) return;   // wave-uniform: no query of this wave sees these keys
+    // both halves' scores, each K operand read once for the two products
+    f32x16 s[2];
+    u32x4 kf = kread(sl, h, 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const u32x4 kc = kf;
+      if (st + 1 < NS) kf = kread(sl, h, st + 1);
+      s[0] = E::mma(kc, qf[0][st], st == 0 ? zero16() : s[0]);
+      s[1] = E::mma(kc, qop(1, st), st == 0 ? zero16() : s[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P of both halves from the stale reference, in place of the scores (as in
+    // fwd_unit_kernel: no row max on the common path)
+    float rs[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      mask(s[f], f, k0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[f][v] = fast_exp2(fmaf(s[f][v], c2, -mr[f]));
+      rs[f] = rowsum(s[f]);
+    }
+    const bool slow0 = __builtin_amdgcn_ballot_w64(!(rs[0] <= TAU_SUM)) != 0;
+    const bool slow1 = __builtin_amdgcn_ballot_w64(!(rs[1] <= TAU_SUM)) != 0;
+    if (slow0 || slow1) {
+      // a half where some lane's P sums past TAU_SUM (or has no reference yet) takes the
+      // slow path of fwd_unit_kernel on its scores formed again (the same products in the
+      // same order, so the same bits; the registers do not keep the scores past the
+      // exponentials): the row max, the reference raised to it, O and the row sum
+      // rescaled, P formed again
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (!(f == 0 ? slow0 : slow1)) continue;
+        f32x16 x;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          x = E::mma(kread(sl, h, st), qop(f, st), st == 0 ? zero16() : x);
+          __builtin_amdgcn_sched_barrier(0);   // one operand read at a time on this rare path
+        }
+        mask(x, f, k0);
+        float mx = x[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+        const float mnew = fmaxf(mr[f], half_max(mx) * c2);
+        const float alpha = fast_exp2(mr[f] - mnew);   // 0 from the sentinel, 1 if unmoved
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[f][e][v] *= alpha;
+        l_run[f] *= alpha;
+        mr[f] = mnew;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[f][v] = fast_exp2(fmaf(x[v], c2, -mr[f]));
+        rs[f] = rowsum(s[f]);
+      }
+    }
+    u32x4 pf[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      l_run[f] += rs[f];
+      pf[f][0] = u32x4{E::pack(s[f][0], s[f][1]), E::pack(s[f][2], s[f][3]), E::pack(s[f][4], s[f][5]),
+                       E::pack(s[f][6], s[f][7])};
+      pf[f][1] = u32x4{E::pack(s[f][8], s[f][9]), E::pack(s[f][10], s[f][11]), E::pack(s[f][12], s[f][13]),
+                       E::pack(s[f][14], s[f][15])};
+    }
+    // O^T += V^T P^T for both halves, each V operand read once for the two products
+    u32x4 vf = vread(sl, h, 0, 0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int k = 0; k < 2 * NE; ++k) {
+      const int t = k / NE, e = k % NE;
+      const u32x4 vc = vf;
+      if (k + 1 < 2 * NE) vf = vread(sl, h, (k + 1) / NE, (k + 1) % NE);
+      o[0][e] = E::mma(vc, pf[0][t], o[0][e]);
+      o[1][e] = E::mma(vc, pf[1][t], o[1][e]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto dma = [&](int j, unsigned char* sl) __attribute__((always_inline)) {
+    Tiles::load(Kg, Vg, N, j, wave, doff, sl);
+  };
+  auto tile = [&](auto Tc, int j) __attribute__((always_inline)) {
+    constexpr int T = decltype(Tc)::value;
+    unsigned char* const sc = slot(T);
+    if (j > 0) {
+      wait_loads();
+      __syncthreads();
+    }
+    if (j + NSL - 1 < ntile) dma(j + NSL - 1, slot((T + NSL - 1) % NSL));
+    unit(2 * j, sc, 0);
+    unit(2 * j + 1, sc, 1);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  dma(0, slot0);
+  if (ntile > 1) dma(1, slot1);
+  wait_loads();
+  __syncthreads();
+  for (int j = 0; j < ntile; j += NSL) {
+    tile(I0{}, j);
+    if (j + 1 >= ntile) break;
+    tile(I1{}, j + 1);
+    if (j + 2 >= ntile) break;
+    tile(I2{}, j + 2);
+  }
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const float l_tot = half_sum(l_run[f]);
+    if (myq[f] < N) {
+      store_row16<E>((unsigned char*)a.o + (qhead + myq[f]) * ROWB, o[f], 1.f / l_tot, hh);
+      if (hh == 0) a.lse[qhead + myq[f]] = (mr[f] + log2f(l_tot)) * kLn2;
+    }
+  }
+}
+
 // Waves per workgroup of fwd_unit_kernel.  d = 64: 8 (two workgroups per CU beat one
 // of 16 at every measured shape).  d = 128: 12, one workgroup of 384 rows per CU; 6
 // (192 rows, two per CU) when the 384-row grid is small — at most 128 workgroups, or
@@ -775,8 +1025,20 @@ static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStre
   return hipGetLastError();
 }
 
+// fa_fwd: at d = 128 the 64-query waves (512-row workgroups, one per CU) once their grid
+// fills the CUs at least twice when causal (the blocks differ in length) or once when
+// not (2-3 % faster causal, 8-10 % not, at N = 8192-16384); smaller grids keep the 32-query
+// kernel, whose smaller workgroups spread the work over more CUs.
 template <class Tag, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128) {
+    constexpr int NW2 = 8;
+    const long long nb = (long long)a.B * a.Hq * ((a.N + 64 * NW2 - 1) / (64 * NW2));
+    if (nb >= (CAUSAL ? 512 : 256)) {
+      hipLaunchKernelGGL((fwd_unit2_kernel<Tag, D, CAUSAL, NW2>), dim3((unsigned)nb), dim3(NW2 * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   return launch_fwd_unit<Tag, D, CAUSAL, false>(a, a.N, CAUSAL, stream);
 }
 
