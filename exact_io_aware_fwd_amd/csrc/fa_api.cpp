@@ -471,8 +471,8 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
     a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * kLog2e;
     hipError_t err;
-    if (p.S == 1) {   // one split: the forward writes O and LSE itself
-      err = fa::launch_fwd_masked(a, (int)d, dtype == FA_BF16, (hipStream_t)stream);
+    if (p.S == 1) {   // one split: fa_fwd itself (the same bits as the general mode without a mask)
+      err = fa::launch_fwd(a, (int)d, dtype == FA_BF16, causal != 0, (hipStream_t)stream);
     } else {
       a.ksplit = p.S;
       a.kchunk = p.C;

@@ -80,6 +80,19 @@ def test_prefill_key_split_matches_fa_fwd_on_a_small_grid():
     assert (l1 - l2).abs().max().item() <= 2e-5
 
 
+@pytest.mark.parametrize("Hq,causal", [(256, False), (16, True)], ids=["q64-waves", "q32-waves"])
+def test_prefill_one_split_is_fa_fwd(Hq, causal):
+    """With one key split the key-split route is fa_fwd itself: the same bits, on a grid
+    where fa_fwd runs 64-query waves (256 query heads, N = 512, non-causal) and on one
+    where it runs 32-query waves."""
+    q, k, v = _inputs(460 + Hq, 1, Hq, Hq // 8, 512, 512, 128, torch.bfloat16)
+    qd, kd, vd = to_dev(q, k, v)
+    o1, l1 = fa.fwd_splitkv(qd, kd, vd, causal=causal, softmax_scale=0.0883883, num_splits=1)
+    o2, l2 = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=0.0883883)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_splitkv_mqa_and_mha():
     q, k, v = _inputs(310, 1, 16, 1, 3, 777, 128, torch.bfloat16)      # MQA: 48 rows -> two row groups
     check_splitkv(q, k, v, True, 0.0883883, label="mqa")
