@@ -766,11 +766,10 @@ fwd_unit2_kernel(const FwdArgs a) {
   constexpr int BR = 64 * NW;
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;
-  constexpr bool SWZ = D == 64;
-  constexpr int PK = SWZ ? ROWB : ROWB + 16;
-  constexpr int PV = SWZ ? ROWB : ROWB + 64;
-  using Tiles = TilePair<ROWB, PK, PV, NW, SWZ, SWZ>;
-  using SO = SwzOffsets<ROWB>;
+  static_assert(D == 128, "at d = 64 the 32-query kernel's four waves per SIMD are faster");
+  constexpr int PK = ROWB + 16;   // padded K and V rows, as in fwd_unit_kernel at d = 128
+  constexpr int PV = ROWB + 64;
+  using Tiles = TilePair<ROWB, PK, PV, NW>;
   constexpr int KBYTES = Tiles::ABYTES;
   constexpr int SLOT = Tiles::SLOT;
   constexpr int IPW = Tiles::IPW;
@@ -833,19 +832,14 @@ fwd_unit2_kernel(const FwdArgs a) {
   for (int f = 0; f < 2; ++f) whi[f] = CAUSAL ? min(qw + 32 * f, N - 1) : N - 1;
   int doff[IPW];
   Tiles::offsets(wave, lane, doff);
-  const int ka = SWZ ? SO::rows_a0(lane) : r32 * PK + 16 * hh;
-  const int va = KBYTES + (SWZ ? SO::tr_lane(lane)
-                               : (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+  const int ka = r32 * PK + 16 * hh;
+  const int va = KBYTES + (4 * hh + ((lane & 15) >> 2)) * PV + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
   auto kread = [&](const unsigned char* sl, int h, int st) __attribute__((always_inline)) {
-    if constexpr (SWZ) return *(const u32x4*)(sl + h * 32 * PK + (ka ^ (st << 5)));
-    else return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
+    return *(const u32x4*)(sl + h * 32 * PK + ka + 32 * st);
   };
   auto vread = [&](const unsigned char* sl, int hv, int h, int e) __attribute__((always_inline)) {
     const unsigned char* p = sl + (32 * hv + 16 * h) * PV;
-    if constexpr (SWZ)
-      return cat(lds_read_tr(p + (va ^ SO::tr_inst(e, 0))), lds_read_tr(p + 8 * PV + (va ^ SO::tr_inst(e, 1))));
-    else
-      return cat(lds_read_tr(p + va + 64 * e), lds_read_tr(p + 8 * PV + va + 64 * e));
+    return cat(lds_read_tr(p + va + 64 * e), lds_read_tr(p + 8 * PV + va + 64 * e));
   };
   const float c2 = a.scale_log2;
   float mr[2] = {-FLT_MAX, -FLT_MAX}, l_run[2] = {0.f, 0.f};
