@@ -50,7 +50,8 @@
 //    some lane of the wave raised it.  fwd_unit_kernel forms no row max at all on its
 //    common path: P comes from the reference as it stands, and only when a lane's
 //    probabilities over the unit sum past 256 (or the lane has no reference yet)
-//    does the wave take the row max, raise the reference and form P again; its
+//    does the wave take the row max, raise the reference (in bf16 to 8 above that max,
+//    so that rising scores come back to this path half as often) and form P again; its
 //    products run at raised wave priority (s_setprio), so a wave entering them is
 //    issued ahead of waves still in their softmax.
 //  * Causal: a workgroup stops at the last tile its rows can see; units no query of a
@@ -499,6 +500,10 @@ fwd_unit_kernel(const FwdArgs a) {
   constexpr int NE = D / 32;
   constexpr int NS = D / 16;
   constexpr float TAU_SUM = 256.f;   // bound on a lane's sum of P over a unit (2^8)
+  // a raised reference sits HEADROOM (log2 units) above the row max that raised it: scores
+  // that keep rising then have to climb about 16 log2 units, not 8, before P's sum passes
+  // TAU_SUM again.  bf16 only: P scaled down that far would reach fp16's subnormal range
+  constexpr float HEADROOM = std::is_same<Tag, bf16_tag>::value ? 8.f : 0.f;
   // NSL LDS slots as distinct objects (see fwd_kernel): three with one workgroup per
   // CU, two where a second workgroup has to fit beside it
   constexpr int NSL = NW >= 12 ? 3 : 2;
@@ -641,8 +646,9 @@ fwd_unit_kernel(const FwdArgs a) {
     // normalised result, it only has to keep P from overflowing.  If this lane's
     // probabilities sum past TAU_SUM = 2^8 (so some P may exceed 2^8, or the lane has no
     // reference yet, whose sentinel -FLT_MAX makes every visible P infinite), the wave
-    // takes the slow path: the row max of the unit, the reference raised to it, O and
-    // the row sum rescaled, P formed again.  Masked scores (-inf) give P = 0 either way.
+    // takes the slow path: the row max of the unit, the reference raised to it (plus
+    // HEADROOM), O and the row sum rescaled, P formed again.  Masked scores (-inf) give
+    // P = 0 either way.
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(s[v], c2, -mr));
@@ -659,7 +665,7 @@ fwd_unit_kernel(const FwdArgs a) {
       float mx = s[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-      const float mnew = fmaxf(mr, half_max(mx) * c2);
+      const float mnew = fmaxf(mr, half_max(mx) * c2 + HEADROOM);
       const float alpha = fast_exp2(mr - mnew);   // 0 from the sentinel, 1 if unmoved
 #pragma unroll
       for (int e = 0; e < NE; ++e)
@@ -776,6 +782,10 @@ fwd_unit2_kernel(const FwdArgs a) {
   constexpr int NE = D / 32;
   constexpr int NS = D / 16;
   constexpr float TAU_SUM = 256.f;   // bound on a lane's sum of P over a unit (2^8)
+  // a raised reference sits HEADROOM (log2 units) above the row max that raised it: scores
+  // that keep rising then have to climb about 16 log2 units, not 8, before P's sum passes
+  // TAU_SUM again.  bf16 only: P scaled down that far would reach fp16's subnormal range
+  constexpr float HEADROOM = std::is_same<Tag, bf16_tag>::value ? 8.f : 0.f;
   constexpr int NSL = 3;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
@@ -900,8 +910,8 @@ fwd_unit2_kernel(const FwdArgs a) {
       // a half where some lane's P sums past TAU_SUM (or has no reference yet) takes the
       // slow path of fwd_unit_kernel on its scores formed again (the same products in the
       // same order, so the same bits; the registers do not keep the scores past the
-      // exponentials): the row max, the reference raised to it, O and the row sum
-      // rescaled, P formed again
+      // exponentials): the row max, the reference raised to it (plus HEADROOM), O and
+      // the row sum rescaled, P formed again
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         if (!(f == 0 ? slow0 : slow1)) continue;
@@ -915,7 +925,7 @@ fwd_unit2_kernel(const FwdArgs a) {
         float mx = x[0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        const float mnew = fmaxf(mr[f], half_max(mx) * c2);
+        const float mnew = fmaxf(mr[f], half_max(mx) * c2 + HEADROOM);
         const float alpha = fast_exp2(mr[f] - mnew);   // 0 from the sentinel, 1 if unmoved
 #pragma unroll
         for (int e = 0; e < NE; ++e)
@@ -979,12 +989,16 @@ fwd_unit2_kernel(const FwdArgs a) {
     if (j + 2 >= ntile) break;
     tile(I2{}, j + 2);
   }
+  // the rows again from the lane number (mbcnt) and the wave's first row, so that no row
+  // index has to stay live across the tile loop for these stores
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const float l_tot = half_sum(l_run[f]);
-    if (myq[f] < N) {
-      store_row16<E>((unsigned char*)a.o + (qhead + myq[f]) * ROWB, o[f], 1.f / l_tot, hh);
-      if (hh == 0) a.lse[qhead + myq[f]] = (mr[f] + log2f(l_tot)) * kLn2;
+    const int row = qw + 32 * f + (lane_e & 31);
+    if (row < N) {
+      store_row16<E>((unsigned char*)a.o + (qhead + row) * ROWB, o[f], 1.f / l_tot, lane_e >> 5);
+      if (lane_e < 32) a.lse[qhead + row] = (mr[f] + log2f(l_tot)) * kLn2;
     }
   }
 }
