@@ -478,11 +478,18 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 // the same at every NW, and a unit that no query of a wave sees (past its diagonal,
 // outside its window) is skipped by that wave, which changes no bit.  GEN: the mask
 // family without block lists (lengths, packed batches, windows) as in fwd_kernel.
-template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false>
+// KS = 2 (small grids): two waves per 32 queries, one taking the first and one the second
+// 32-key unit of every tile, their O, row sums and references merged through LDS at the
+// end (the online softmax's merge of two partial results, "FlashAttention Primer",
+// "FlashAttention-1"; the key split of Flash-Decoding, "Flash Attention" wiki), so a
+// block's chain of units is half as long and its rows spread over twice the workgroups.
+template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false, int KS = 1>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4)))
 fwd_unit_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
-  constexpr int BR = 32 * NW;
+  static_assert(KS == 1 || KS == 2, "one or two waves per 32 queries");
+  constexpr int RG = NW / KS;   // 32-query row groups of the workgroup
+  constexpr int BR = 32 * RG;
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;
   // K and V tiles free of bank conflicts for the row reads of K and the transposing reads
@@ -505,8 +512,9 @@ fwd_unit_kernel(const FwdArgs a) {
   // TAU_SUM again.  bf16 only: P scaled down that far would reach fp16's subnormal range
   constexpr float HEADROOM = std::is_same<Tag, bf16_tag>::value ? 8.f : 0.f;
   // NSL LDS slots as distinct objects (see fwd_kernel): three with one workgroup per
-  // CU, two where a second workgroup has to fit beside it
-  constexpr int NSL = NW >= 12 ? 3 : 2;
+  // CU (12 waves, or the key-split workgroups of small grids), two where a second
+  // workgroup has to fit beside it
+  constexpr int NSL = (NW >= 12 || KS == 2) ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) unsigned char slot0[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char slot1[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned char slot2[NSL == 3 ? SLOT : 1];
@@ -515,6 +523,8 @@ fwd_unit_kernel(const FwdArgs a) {
   };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rgw = KS == 1 ? wave : wave % RG;   // this wave's row group
+  const int kh = KS == 1 ? 0 : wave / RG;       // KS = 2: the unit of each tile it takes
   const int hh = lane >> 5, r32 = lane & 31;
   const int N = a.N;
   int b, hq, iq;
@@ -548,7 +558,7 @@ fwd_unit_kernel(const FwdArgs a) {
   const unsigned char* Vg = (const unsigned char*)a.v + kvhead * ROWB;
   const int q0 = iq * BR;
   if (GEN && q0 >= Lq) return;   // the whole workgroup: past this sequence's queries
-  const int qw = q0 + wave * 32;
+  const int qw = q0 + rgw * 32;
   const int myq = qw + r32;
   u32x4 qf[NS];
   if (myq < Lq) {
@@ -706,8 +716,12 @@ fwd_unit_kernel(const FwdArgs a) {
       __syncthreads();   // everyone's; everyone is done with tile j-1
     }
     if (j + NSL - 1 < ntile) dma(j + NSL - 1, slot((T + NSL - 1) % NSL));
-    unit(2 * (t_lo + j), sc, 0);
-    unit(2 * (t_lo + j) + 1, sc, 1);
+    if constexpr (KS == 1) {
+      unit(2 * (t_lo + j), sc, 0);
+      unit(2 * (t_lo + j) + 1, sc, 1);
+    } else {
+      unit(2 * (t_lo + j) + kh, sc, kh);
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -726,6 +740,34 @@ fwd_unit_kernel(const FwdArgs a) {
         tile(I2{}, j + 2);
       }
     }
+  }
+  if constexpr (KS == 2) {
+    // the second-unit wave hands its O^T, reference and row sum (lane for lane: both
+    // waves hold the same rows in the same layout) to the first, which rescales both to
+    // the larger reference and adds them; two row groups' records per LDS slot
+    constexpr int REC = (NE * 16 + 2) * 64;   // floats
+    static_assert(RG <= 2 * NSL && 2 * REC * 4 <= SLOT, "two merge records per slot");
+    __syncthreads();   // every wave is done with the last tile
+    float* const rec = (float*)slot(rgw >> 1) + (rgw & 1) * REC + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) rec[(16 * e + v) * 64] = o[e][v];
+      rec[NE * 16 * 64] = mr;
+      rec[(NE * 16 + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = rec[NE * 16 * 64], l1 = rec[(NE * 16 + 1) * 64];
+    const float mm = fmaxf(mr, m1);
+    const float a0 = fast_exp2(mr - mm), a1 = fast_exp2(m1 - mm);   // 0 for a part with no key
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[e][v] = o[e][v] * a0 + rec[(16 * e + v) * 64] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    mr = mm;
   }
   // epilogue: O = O^T / l, LSE = ln(2) * (m + log2 l); a row that saw no key (mask
   // family only) gets O = 0 and LSE = -inf
@@ -1008,16 +1050,37 @@ fwd_unit2_kernel(const FwdArgs a) {
 // (192 rows, two per CU) when the 384-row grid is small — at most 128 workgroups, or
 // 256 when causal, where a single long diagonal block would otherwise set the time.
 // Past that the 6-wave grid loses: two workgroups per CU load every K/V tile twice.
+// (Without key splits, the smallest d = 128 grids take the key-split workgroups below.)
 template <int D>
 static int fwd_unit_waves(long long rows_blocks_of_384, bool causal) {
   if (D != 128) return 8;
   return rows_blocks_of_384 <= (causal ? 256 : 128) ? 6 : 12;
 }
 
+// d = 128 small grids, no key splits: 8 waves on 128 rows, two per 32 queries each taking
+// one 32-key unit of every tile (KS = 2), while the 128-row grid fits the CUs once (256
+// workgroups) or, causal, twice (its blocks differ in length).  A block's chain of units
+// halves and its rows spread over more workgroups: 1.15-1.55x faster at one sequence of
+// 1-8K tokens (16 heads of 1024 causal 29 -> 23 us, of 2048 50 -> 37 us, 4 heads of 8192
+// causal 188 -> 119 us); on 768 or more blocks (384 non-causal) it was 8-27 % slower.
+static bool fwd_small_grid_split(long long rows_blocks_of_128, bool causal) {
+  return rows_blocks_of_128 <= (causal ? 512 : 256);
+}
+
 template <class Tag, int D, bool CAUSAL, bool GEN>
 static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStream_t stream) {
   const long long bh = (long long)a.B * a.Hq;
   const int ks = GEN ? a.ksplit : 1;   // key splits multiply the grid
+  if constexpr (D == 128) {
+    if (ks == 1 && fwd_small_grid_split(bh * ((nq + 127) / 128), causal)) {
+      constexpr int NWS = 8, BRS = 32 * NWS / 2;
+      const long long nb = bh * ((nq + BRS - 1) / BRS);
+      if (nb <= 0) return hipSuccess;
+      hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, NWS, GEN, 2>), dim3((unsigned)nb), dim3(NWS * 64), 0, stream,
+                         a);
+      return hipGetLastError();
+    }
+  }
   const int nw = fwd_unit_waves<D>(bh * ((nq + 383) / 384) * ks, causal);
   const int br = 32 * nw;
   const long long nb = bh * ((nq + br - 1) / br) * ks;

@@ -69,22 +69,23 @@ def test_prefill_key_split(dtype, d, B, Hq, Hkv, N, causal, S):
 
 
 def test_prefill_key_split_matches_fa_fwd_on_a_small_grid():
-    """The key-split route against fa_fwd on the shape it is for (one sequence of 1024
-    tokens, 32 query heads over 8 K/V heads): both within the oracle's tolerance, and
-    within the bf16 output rounding of each other."""
+    """Two key splits against fa_fwd on a small grid (one sequence of 1024 tokens, 32
+    query heads over 8 K/V heads): both within the oracle's tolerance, and within the
+    bf16 output rounding of each other; at d = 128 the default is one split (fa_fwd)."""
     q, k, v = _inputs(450, 1, 32, 8, 1024, 1024, 128, torch.bfloat16)
-    o1, l1 = check_splitkv(q, k, v, True, 0.0883883, label="small grid")
+    assert fa.splitkv_num_splits(1, 32, 8, 1024, 1024, 128) == 1
+    o1, l1 = check_splitkv(q, k, v, True, 0.0883883, num_splits=2, label="small grid")
     o2, l2 = fa.fwd(*to_dev(q, k, v), causal=True, softmax_scale=0.0883883)
     torch.cuda.synchronize()
     assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -7 * o2.float().abs().max().item()
     assert (l1 - l2).abs().max().item() <= 2e-5
 
 
-@pytest.mark.parametrize("Hq,causal", [(256, False), (16, True)], ids=["q64-waves", "q32-waves"])
+@pytest.mark.parametrize("Hq,causal", [(256, False), (16, True)], ids=["q64-waves", "small-grid"])
 def test_prefill_one_split_is_fa_fwd(Hq, causal):
     """With one key split the key-split route is fa_fwd itself: the same bits, on a grid
-    where fa_fwd runs 64-query waves (256 query heads, N = 512, non-causal) and on one
-    where it runs 32-query waves."""
+    where fa_fwd runs 64-query waves (256 query heads, N = 512, non-causal) and on a small
+    one (16 heads, causal) where it runs two waves per 32 queries."""
     q, k, v = _inputs(460 + Hq, 1, Hq, Hq // 8, 512, 512, 128, torch.bfloat16)
     qd, kd, vd = to_dev(q, k, v)
     o1, l1 = fa.fwd_splitkv(qd, kd, vd, causal=causal, softmax_scale=0.0883883, num_splits=1)

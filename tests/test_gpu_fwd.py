@@ -109,25 +109,56 @@ def test_gqa_head_mapping():
             assert torch.all(o[b, h] == float(b * Hkv + h // (Hq // Hkv))), (b, h)
 
 
-@pytest.mark.parametrize("causal,hq", [(False, 128), (True, 256)])
-def test_workgroup_shape_does_not_change_bits(causal, hq):
-    """At d = 128 the forward runs 6-wave (192-row) workgroups when the 384-row grid is
-    small (at most 128 blocks, 256 when causal) and 12-wave ones otherwise.  One more
-    query head crosses that line: the heads both calls share must come out bit for bit
-    the same, and the oracle checks the first and the extra head of the larger call."""
+def small_grid_split(B, Hq, N, d, causal):
+    """The launch rule of fa_fwd at d = 128: grids of at most 256 blocks of 128 rows (512
+    when causal) run the key-split workgroups (8 waves, two per 32 queries)."""
+    return d == 128 and B * Hq * -(-N // 128) <= (512 if causal else 256)
+
+
+@pytest.mark.parametrize("causal,hq", [(False, 85), (True, 170)])
+def test_small_grid_key_split_threshold(causal, hq):
+    """One more query head takes the grid past the small-grid line: the smaller call runs
+    the key-split workgroups (each 32 queries' two waves take alternate 32-key units and
+    merge their partial results, "FlashAttention Primer", "FlashAttention-1"), the larger
+    one wave per 32 queries.  The two sum in different orders, so the heads they share
+    agree to rounding, not bit for bit; the oracle checks the first and last head of each."""
     N, d = 300, 128
+    assert small_grid_split(1, hq, N, d, causal) and not small_grid_split(1, hq + 1, N, d, causal)
     q, k, v = workloads.random_case(31 + hq, 1, hq + 1, 1, N, d, torch.bfloat16)
     scale = 1 / math.sqrt(d)
-    say(f"[fwd] workgroup shape: Hq={hq} vs {hq + 1} (MQA) N={N} causal={causal}")
+    say(f"[fwd] small-grid key split: Hq={hq} vs {hq + 1} (MQA) N={N} causal={causal}")
+    qd, kd, vd = to_dev(q, k, v)
+    o_small, l_small = fa.fwd(qd[:, :hq].contiguous(), kd, vd, causal=causal, softmax_scale=scale)
+    o_big, l_big = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+    torch.cuda.synchronize()
+    for o, l, heads in ((o_small, l_small, (0, hq - 1)), (o_big, l_big, (0, hq))):
+        for h in heads:
+            O_ref, L_ref = oracle.attention_fwd(q[:, h:h + 1], k, v, causal, scale)
+            eo, el = o_err(o[:, h:h + 1].cpu(), O_ref), lse_err(l[:, h:h + 1].cpu(), L_ref)
+            say(f"    Hq={o.shape[1]} head {h}: O {eo:.2e} LSE {el:.2e}")
+            assert eo <= O_TOL[torch.bfloat16] and el <= LSE_TOL
+    ref = o_big[:, :hq].float()
+    assert (o_small.float() - ref).abs().max().item() <= O_TOL[torch.bfloat16] * ref.abs().max().item()
+    assert (l_small - l_big[:, :hq]).abs().max().item() <= LSE_TOL
+
+
+@pytest.mark.parametrize("causal,hq", [(False, 64), (True, 128)])
+def test_key_split_grid_does_not_change_bits(causal, hq):
+    """Inside the small-grid region every row takes the same steps whatever the grid, so
+    one more query head leaves the heads both calls share bit for bit the same."""
+    N, d = 300, 128
+    assert small_grid_split(1, hq, N, d, causal) and small_grid_split(1, hq + 1, N, d, causal)
+    q, k, v = workloads.random_case(41 + hq, 1, hq + 1, 1, N, d, torch.float16)
+    scale = 1 / math.sqrt(d)
+    say(f"[fwd] key-split grid: Hq={hq} vs {hq + 1} (MQA) N={N} causal={causal}")
     qd, kd, vd = to_dev(q, k, v)
     o_small, l_small = fa.fwd(qd[:, :hq].contiguous(), kd, vd, causal=causal, softmax_scale=scale)
     o_big, l_big = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o_small, o_big[:, :hq]) and torch.equal(l_small, l_big[:, :hq])
-    for h in (0, hq):
-        O_ref, L_ref = oracle.attention_fwd(q[:, h:h + 1], k, v, causal, scale)
-        assert o_err(o_big[:, h:h + 1].cpu(), O_ref) <= O_TOL[torch.bfloat16]
-        assert np.abs(l_big[:, h:h + 1].cpu().double().numpy() - L_ref).max() <= LSE_TOL
+    O_ref, L_ref = oracle.attention_fwd(q[:, hq:hq + 1], k, v, causal, scale)
+    assert o_err(o_big[:, hq:hq + 1].cpu(), O_ref) <= O_TOL[torch.float16]
+    assert lse_err(l_big[:, hq:hq + 1].cpu(), L_ref) <= LSE_TOL
 
 
 def test_forward_is_bitwise_deterministic():
