@@ -744,11 +744,12 @@ fwd_unit_kernel(const FwdArgs a) {
   if constexpr (KS == 2) {
     // the second-unit wave hands its O^T, reference and row sum (lane for lane: both
     // waves hold the same rows in the same layout) to the first, which rescales both to
-    // the larger reference and adds them; two row groups' records per LDS slot
+    // the larger reference and adds them; as many row groups' records per LDS slot as fit
     constexpr int REC = (NE * 16 + 2) * 64;   // floats
-    static_assert(RG <= 2 * NSL && 2 * REC * 4 <= SLOT, "two merge records per slot");
+    constexpr int RPS = SLOT / (REC * 4);     // records per slot
+    static_assert(RPS >= 1 && RG <= RPS * NSL, "the merge records fit the slots");
     __syncthreads();   // every wave is done with the last tile
-    float* const rec = (float*)slot(rgw >> 1) + (rgw & 1) * REC + lane;
+    float* const rec = (float*)slot((unsigned)rgw / RPS) + ((unsigned)rgw % RPS) * REC + lane;
     if (kh == 1) {
 #pragma unroll
       for (int e = 0; e < NE; ++e)
@@ -1050,7 +1051,7 @@ fwd_unit2_kernel(const FwdArgs a) {
 // (192 rows, two per CU) when the 384-row grid is small — at most 128 workgroups, or
 // 256 when causal, where a single long diagonal block would otherwise set the time.
 // Past that the 6-wave grid loses: two workgroups per CU load every K/V tile twice.
-// (Without key splits, the smallest d = 128 grids take the key-split workgroups below.)
+// (Without key splits, the smallest grids take the key-split workgroups below.)
 template <int D>
 static int fwd_unit_waves(long long rows_blocks_of_384, bool causal) {
   if (D != 128) return 8;
@@ -1066,6 +1067,16 @@ static int fwd_unit_waves(long long rows_blocks_of_384, bool causal) {
 static bool fwd_small_grid_split(long long rows_blocks_of_128, bool causal) {
   return rows_blocks_of_128 <= (causal ? 512 : 256);
 }
+// d = 64 (where a CU holds more, smaller workgroups): 4 waves on 64 rows while the 64-row
+// grid has at most 512 blocks, 6 waves on 96 rows for causal grids of up to 1024 such
+// blocks, else the 8-wave grid (measured: 16 heads of 1024 causal 21.4 -> 16.2 us, of 4096
+// causal 66.8 -> 51.0 us; 4 heads over one K/V head at 8192 causal 126 -> 87 us; past these
+// limits 10-50 % slower).  0: no split.
+static int fwd_small_grid_split_waves_d64(long long rows_blocks_of_64, bool causal) {
+  if (rows_blocks_of_64 <= 512) return 4;
+  if (causal && rows_blocks_of_64 <= 1024) return 6;
+  return 0;
+}
 
 template <class Tag, int D, bool CAUSAL, bool GEN>
 static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStream_t stream) {
@@ -1078,6 +1089,18 @@ static hipError_t launch_fwd_unit(const FwdArgs& a, int nq, bool causal, hipStre
       if (nb <= 0) return hipSuccess;
       hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, NWS, GEN, 2>), dim3((unsigned)nb), dim3(NWS * 64), 0, stream,
                          a);
+      return hipGetLastError();
+    }
+  } else {
+    const int nws = ks == 1 ? fwd_small_grid_split_waves_d64(bh * ((nq + 63) / 64), causal) : 0;
+    if (nws != 0) {
+      const int brs = 16 * nws;
+      const long long nb = bh * ((nq + brs - 1) / brs);
+      if (nb <= 0) return hipSuccess;
+      if (nws == 4)
+        hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, 4, GEN, 2>), dim3((unsigned)nb), dim3(4 * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_unit_kernel<Tag, D, CAUSAL, 6, GEN, 2>), dim3((unsigned)nb), dim3(6 * 64), 0, stream, a);
       return hipGetLastError();
     }
   }

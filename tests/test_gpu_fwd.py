@@ -161,6 +161,30 @@ def test_key_split_grid_does_not_change_bits(causal, hq):
     assert lse_err(l_big[:, hq:hq + 1].cpu(), L_ref) <= LSE_TOL
 
 
+def small_grid_waves_d64(B, Hq, N, causal):
+    """The launch rule of fa_fwd at d = 64: 4 waves on 64 rows while the 64-row grid has at
+    most 512 blocks, 6 on 96 rows for causal grids of up to 1024, else none (8-wave grid)."""
+    nb = B * Hq * -(-N // 64)
+    return 4 if nb <= 512 else 6 if causal and nb <= 1024 else 0
+
+
+@pytest.mark.parametrize("case", [
+    # (B, Hq, Hkv, N, dtype, causal, waves per workgroup the rule picks)
+    (1, 12, 4, 3000, torch.float16, True, 6),
+    (2, 4, 1, 2049, torch.bfloat16, True, 4),
+    (1, 16, 16, 1111, torch.bfloat16, False, 4),
+    (1, 3, 3, 4100, torch.float16, False, 4),
+], ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}N{c[3]}{'f16' if c[4] == torch.float16 else 'bf16'}"
+                 f"{'causal' if c[5] else 'full'}-{c[6]}w")
+def test_small_grid_key_split_d64(case):
+    """d = 64 small grids run the same two-waves-per-32-queries workgroups (64 or 96 rows):
+    whole tensors against the oracle, ragged tails, GQA/MQA."""
+    B, Hq, Hkv, N, dt, causal, nw = case
+    assert small_grid_waves_d64(B, Hq, N, causal) == nw
+    q, k, v = workloads.random_case(5100 + N + Hq, B, Hq, Hkv, N, 64, dt)
+    check_fwd(q, k, v, causal, 0.125, label=f"d=64 key-split {nw} waves")
+
+
 def test_forward_is_bitwise_deterministic():
     w = workloads.WORKLOADS["b4_h32_n4096_d128_bf16_causal_qx8"]
     q, k, v = to_dev(*workloads.random_case(9, 2, 8, 2, 2048, 128, torch.bfloat16))
