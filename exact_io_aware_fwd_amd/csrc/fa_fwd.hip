@@ -483,12 +483,17 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 // end (the online softmax's merge of two partial results, "FlashAttention Primer",
 // "FlashAttention-1"; the key split of Flash-Decoding, "Flash Attention" wiki), so a
 // block's chain of units is half as long and its rows spread over twice the workgroups.
+// The d = 64 4-wave form of it (two workgroups per CU, one wave per SIMD each) reads every
+// K and V operand of a unit before its products, with the registers of two waves per SIMD
+// (12-17 % faster there; no gain at d = 128, and the 6-wave form would spill).
+constexpr int unit_waves_per_eu(int d, int nw, int ks) { return (ks == 2 && d == 64 && nw == 4) ? 2 : d == 128 ? 3 : 4; }
 template <class Tag, int D, bool CAUSAL, int NW, bool GEN = false, int KS = 1>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 4)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(unit_waves_per_eu(D, NW, KS))))
 fwd_unit_kernel(const FwdArgs a) {
   using E = Elt<Tag>;
   static_assert(KS == 1 || KS == 2, "one or two waves per 32 queries");
   constexpr int RG = NW / KS;   // 32-query row groups of the workgroup
+  constexpr bool PREREAD = KS == 2 && D == 64 && NW == 4;   // all operands of a unit up front
   constexpr int BR = 32 * RG;
   constexpr int BC = 64;
   constexpr int ROWB = D * 2;
@@ -634,14 +639,26 @@ fwd_unit_kernel(const FwdArgs a) {
     const int k0 = u * 32;
     if (k0 > uhi || k0 + 31 < ulo) return;   // wave-uniform: no query of this wave sees these keys
     f32x16 s;
-    u32x4 kf = kread(sl, h, 0);
+    u32x4 vall[PREREAD ? 2 * NE : 1];
+    u32x4 vf;
+    if constexpr (PREREAD) {
+      u32x4 kall[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const u32x4 kc = kf;
-      if (st + 1 < NS) kf = kread(sl, h, st + 1);
-      s = E::mma(kc, qf[st], st == 0 ? zero16() : s);
+      for (int st = 0; st < NS; ++st) kall[st] = kread(sl, h, st);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) s = E::mma(kall[st], qf[st], st == 0 ? zero16() : s);
+#pragma unroll
+      for (int k = 0; k < 2 * NE; ++k) vall[k] = vread(sl, h, k / NE, k % NE);
+    } else {
+      u32x4 kf = kread(sl, h, 0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 kc = kf;
+        if (st + 1 < NS) kf = kread(sl, h, st + 1);
+        s = E::mma(kc, qf[st], st == 0 ? zero16() : s);
+      }
+      vf = vread(sl, h, 0, 0);   // first PV operand, read while the scores settle
     }
-    u32x4 vf = vread(sl, h, 0, 0);   // first PV operand, read while the scores settle
     if (!(k0 >= wlo && k0 + 31 <= whi)) {   // keys outside this lane's window or past the end: -inf
       int lim = (GEN ? min(Lk, hi_q + 1) : N) - k0 - 4 * hh;
       if (!GEN && CAUSAL) lim = min(lim, myq - k0 - 4 * hh + 1);
@@ -694,12 +711,17 @@ fwd_unit_kernel(const FwdArgs a) {
     // the products go first on the SIMD: a wave entering them takes the issue slots from
     // waves still in their softmax, which keeps the matrix core fed
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (PREREAD) {
 #pragma unroll
-    for (int k = 0; k < 2 * NE; ++k) {
-      const int t = k / NE, e = k % NE;
-      const u32x4 vc = vf;
-      if (k + 1 < 2 * NE) vf = vread(sl, h, (k + 1) / NE, (k + 1) % NE);
-      o[e] = E::mma(vc, pf[t], o[e]);
+      for (int k = 0; k < 2 * NE; ++k) o[k % NE] = E::mma(vall[k], pf[k / NE], o[k % NE]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2 * NE; ++k) {
+        const int t = k / NE, e = k % NE;
+        const u32x4 vc = vf;
+        if (k + 1 < 2 * NE) vf = vread(sl, h, (k + 1) / NE, (k + 1) % NE);
+        o[e] = E::mma(vc, pf[t], o[e]);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
