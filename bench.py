@@ -193,8 +193,10 @@ def record_traffic(kdir, cdir, substr):
     kib = COPY_BYTES / 1024
     fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
     write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
+    # the mask family runs fwd_unit_kernel with its general mode on (fifth template argument)
+    targs = substr[substr.find("<") + 1:substr.rfind(">")].split(", ") if "fwd_unit_kernel<" in substr else []
     kind = ("decode" if ("splitkv" in substr or "combine" in substr) else "fp8" if "fp8" in substr
-            else "masks" if "true>" in substr else "bwd" if "bwd" in substr else "fwd")
+            else "masks" if len(targs) >= 5 and targs[4] == "true" else "bwd" if "bwd" in substr else "fwd")
     data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
                   "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
@@ -511,7 +513,7 @@ def bench_masks(args):
         "passes": passes,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": metrics.MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / metrics.MFMA_BF16_TFLOPS, "traffic": traffic_bytes("masks"),
-                     "kernel": "fwd_unit_kernel<bf16, 128, false, 12, true>", "avg_ms": ms, "algorithmic_flops": flops},
+                     "kernel": "fwd_unit_kernel<bf16, 128, false, 12, true, 1>", "avg_ms": ms, "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:
         try:
