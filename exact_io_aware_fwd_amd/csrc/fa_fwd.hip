@@ -22,7 +22,9 @@
 //    waves on its SIMD overlap its softmax with their products: at d = 128 12 waves (one
 //    workgroup per CU, three waves per SIMD), or 6 (two workgroups per CU) when the
 //    384-row grid would leave CUs idle; at d = 64 8 waves, two workgroups per CU (four
-//    waves per SIMD).
+//    waves per SIMD).  On the smallest grids (no key split asked for) it runs two waves
+//    per 32 queries, each taking one 32-key unit of every tile, merged at the end: 8
+//    waves on 128 rows at d = 128, 4 on 64 or 6 on 96 rows at d = 64.
 //  * fwd_kernel (the mask family, fa_fwd_masked): 8 waves x 32 rows (256-row blocks,
 //    the granularity of the block lists), two waves per SIMD, with a software
 //    pipeline per wave: the products S_{u+1} = K_{u+1} Q^T are issued while the
