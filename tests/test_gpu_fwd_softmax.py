@@ -112,3 +112,30 @@ def test_jump_past_the_exponent_range_hits_every_row():
     assert o_err(o.cpu(), O_ref) <= O_TOL[dt] and lse_err(lse.cpu(), L_ref) <= LSE_TOL
     # rows at and after the jump key: O is that key's V (bf16-rounded), LSE its score
     assert torch.equal(o[0, :, jk:].cpu(), v[0, 0, jk].expand(Hq, N - jk, d))
+
+
+@pytest.mark.parametrize("N", [960, 1000], ids=["jump-in-odd-unit", "jump-in-even-unit"])
+def test_small_grid_merge_with_a_jump(N):
+    """On a small grid each 32 queries' keys are split between two waves by 32-key unit
+    parity and the two partial results merged at the end; the jump key (5N/6) lands in an
+    odd unit for N = 960 and an even one for N = 1000, so either wave holds the term that
+    dominates and the other's part must vanish in the merge: O of the rows that see the
+    jump is that key's V exactly, and all rows match the oracle."""
+    B, Hq, Hkv, d, dt = 1, 2, 1, 128, torch.bfloat16
+    jk = (5 * N) // 6
+    assert (jk // 32) % 2 == (1 if N == 960 else 0)
+    q, k, v = _case("jump", B, Hq, Hkv, N, d, dt, 9960 + N)
+    scale = 1 / math.sqrt(d)
+    S = scale * q.double()[0] @ k.double()[0, 0].T
+    others = torch.cat([S[..., :jk], S[..., jk + 1:]], dim=-1).amax(dim=-1)
+    assert torch.all((S[..., jk] - others) * math.log2(math.e) > 128)
+    say(f"[fwd softmax] small-grid merge, jump key {jk} (unit {jk // 32}) N={N}")
+    qd, kd, vd = to_dev(q, k, v)
+    for causal in (True, False):
+        o, lse = fa.fwd(qd, kd, vd, causal=causal, softmax_scale=scale)
+        torch.cuda.synchronize()
+        O_ref, L_ref = oracle.attention_fwd(q, k, v, causal, scale)
+        assert o_err(o.cpu(), O_ref) <= O_TOL[dt] and lse_err(lse.cpu(), L_ref) <= LSE_TOL
+        rows = slice(jk, None) if causal else slice(None)
+        n = o[0, :, rows].shape[1]
+        assert torch.equal(o[0, :, rows].cpu(), v[0, 0, jk].expand(Hq, n, d))
