@@ -476,15 +476,15 @@ __global__ void __launch_bounds__(512) fwd_kernel(const FwdArgs a) {
 // at d = 64) two LDS slots (75 KB at d = 128, 43 KB at d = 64) leave room for a
 // second workgroup per CU; at 12 three slots keep two tiles in flight.  Same tiles,
 // loads, layouts and epilogue as fwd_kernel; the reference max is kept differently
-// (above), so the two kernels agree to rounding, not bit for bit.  The arithmetic is
-// the same at every NW, and a unit that no query of a wave sees (past its diagonal,
+// (above), so the two kernels agree to rounding, not bit for bit.  With KS = 1 the
+// arithmetic is the same at every NW, and a unit that no query of a wave sees (past its diagonal,
 // outside its window) is skipped by that wave, which changes no bit.  GEN: the mask
 // family without block lists (lengths, packed batches, windows) as in fwd_kernel.
 // KS = 2 (small grids): two waves per 32 queries, one taking the first and one the second
 // 32-key unit of every tile, their O, row sums and references merged through LDS at the
 // end (the online softmax's merge of two partial results, "FlashAttention Primer",
 // "FlashAttention-1"; the key split of Flash-Decoding, "Flash Attention" wiki), so a
-// block's chain of units is half as long and its rows spread over twice the workgroups.
+// block's chain of units is half as long and its rows spread over more, smaller workgroups.
 // The d = 64 4-wave form of it (two workgroups per CU, one wave per SIMD each) reads every
 // K and V operand of a unit before its products, with the registers of two waves per SIMD
 // (12-17 % faster there; no gain at d = 128, and the 6-wave form would spill).
