@@ -64,6 +64,12 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *   B >= 0, N >= 0 (either 0: nothing to do, FA_OK); Hq >= 1, Hkv >= 1, Hq % Hkv == 0;
  *   d in {64, 128}; softmax_scale finite and > 0 (callers normally pass 1/sqrt(d)).
  * Returns FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ * The same call gives the same bits every time.  The bits of one head do not depend on
+ * the other heads or batches of the call, except across the small-grid rule: grids of at
+ * most 256 blocks of 128 rows (512 when causal; at d = 64 blocks of 64 rows, 512 or, causal,
+ * 1024) give each 32 queries two waves that take alternate 32-key units and add their
+ * halves at the end, which rounds differently from one wave per 32 queries (both within
+ * the tolerances of the exact result).
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
