@@ -538,9 +538,12 @@ def bench_masks(args):
 def _fwd_kernel(B, Hq, N, d, causal):
     """The forward kernel fa_fwd launches for these sizes (its choice, restated for the
     label): 64-query waves at d = 128 once B * Hq * ceil(N / 512) reaches 512 (causal) or
-    256, else 32-query waves."""
-    return ("fwd_unit2_kernel" if d == 128 and B * Hq * -(-N // 512) >= (512 if causal else 256)
-            else "fwd_unit_kernel")
+    256; two waves per 32 queries on the smallest grids; else one 32-query wave each."""
+    if d == 128 and B * Hq * -(-N // 512) >= (512 if causal else 256):
+        return "fwd_unit2_kernel"
+    small = (B * Hq * -(-N // 128) <= (512 if causal else 256) if d == 128
+             else B * Hq * -(-N // 64) <= (1024 if causal else 512))
+    return "fwd_unit_kernel (two waves per 32 queries)" if small else "fwd_unit_kernel"
 
 
 def _dkdv_kernels(B, Hq, Hkv, N, causal):
@@ -728,8 +731,10 @@ def main():
                          "tflops_median": f_bwd / (med(bwd_t) * 1e-3) / 1e12}
         passes["bwd"]["frac"] = passes["bwd"]["tflops"] / peak
     def roofline(kind):
+        # the recorded counters are the headline workload's: other workloads get none
+        traffic = traffic_bytes(kind) if w.name == workloads.HEADLINE else None
         return {"bound": "mfma", "achieved": passes[kind]["tflops"], "peak": peak, "unit": "TFLOP/s",
-                "frac": passes[kind]["frac"], "traffic": traffic_bytes(kind), "kernel": passes[kind]["kernel"],
+                "frac": passes[kind]["frac"], "traffic": traffic, "kernel": passes[kind]["kernel"],
                 "per_launch_flops": f_fwd if kind == "fwd" else f_bwd, "avg_ms": passes[kind]["ms"],
                 "median_ms": passes[kind]["median_ms"], "min_ms": passes[kind]["min_ms"],
                 "algorithmic_bytes": (metrics.fwd_bytes if kind == "fwd" else metrics.bwd_bytes)(
@@ -739,7 +744,8 @@ def main():
 
     dt_name = {torch.bfloat16: "bf16", torch.float16: "fp16"}[q.dtype]
     rec = {
-        "metric": "attention fwd/bwd TFLOPS and % MFMA peak at N=8192 d=128 bf16 causal",
+        "metric": f"attention fwd/bwd TFLOPS and % MFMA peak at N={w.N} d={w.d} {dt_name} "
+                  f"{'causal' if causal else 'non-causal'}",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dt_name, "data": "synthetic (seeded iid N(0,1))",
