@@ -95,7 +95,7 @@ fa_status check_splitkv_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   if (causal && Nq > Nk)
     return fail(FA_ERR_INVALID_ARGUMENT, "causal needs Nq <= Nk (Nq=%lld Nk=%lld)", (long long)Nq, (long long)Nk);
   if (fa::splitkv_is_prefill(Nq, Nk)) {
-    const fa::PrefillSplit p = fa::plan_prefill_split(B, Hq, Nq, d, num_splits);
+    const fa::PrefillSplit p = fa::plan_prefill_split(Nq, num_splits);
     if (B * Hq * ((Nq + 191) / 192) * p.S > (int64_t)UINT_MAX || Nq * d > INT_MAX)
       return fail(FA_ERR_INVALID_ARGUMENT, "grid size exceeds the launch limit");
     return FA_OK;
@@ -421,14 +421,14 @@ size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, dtype, 0, num_splits, &empty) != FA_OK) return 0;
   if (empty) return 0;
   if (fa::splitkv_is_prefill(Nq, Nk))
-    return fa::prefill_workspace_bytes(B, Hq, Nq, d, fa::plan_prefill_split(B, Hq, Nq, d, num_splits));
+    return fa::prefill_workspace_bytes(B, Hq, Nq, d, fa::plan_prefill_split(Nq, num_splits));
   return fa::splitkv_workspace_bytes(B, Hq, Nq, d, fa::plan_splits(B, Hq, Hkv, Nq, Nk, num_splits));
 }
 
 int64_t fa_fwd_splitkv_num_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
   bool empty = false;
   if (check_splitkv_sizes(B, Hq, Hkv, Nq, Nk, d, FA_BF16, 0, 0, &empty) != FA_OK || empty) return 0;
-  if (fa::splitkv_is_prefill(Nq, Nk)) return fa::plan_prefill_split(B, Hq, Nq, d, 0).S;
+  if (fa::splitkv_is_prefill(Nq, Nk)) return fa::plan_prefill_split(Nq, 0).S;
   const fa::SplitPlan p = fa::plan_splits(B, Hq, Hkv, Nq, Nk, 0);
   return (Nk + p.C - 1) / p.C;
 }
@@ -448,7 +448,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
       (st = check_ptr(lse, "lse")) != FA_OK || (st = check_ptr(workspace, "workspace")) != FA_OK)
     return st;
   if (fa::splitkv_is_prefill(Nq, Nk)) {   // as many queries as keys: key-split prefill
-    const fa::PrefillSplit p = fa::plan_prefill_split(B, Hq, Nq, d, num_splits);
+    const fa::PrefillSplit p = fa::plan_prefill_split(Nq, num_splits);
     const size_t need = fa::prefill_workspace_bytes(B, Hq, Nq, d, p);
     if (workspace_bytes < need)
       return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,

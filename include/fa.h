@@ -140,9 +140,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  * sequence, few heads).  Every query block of fa_fwd's forward is computed by
  * num_splits workgroups, each over a contiguous range of 64-key tiles, and the parts are
  * merged by the same log-sum-exp combine; num_splits then counts splits per query block
- * and the split size is rounded to 64 keys.  Default: one split (fa_fwd itself) at
- * d = 128, whose small grids already split each block's keys between two waves; at
- * d = 64 two while B * Hq * ceil(N / 192) <= 128, else one.
+ * and the split size is rounded to 64 keys.  Default: one split (fa_fwd itself), whose
+ * small grids already split each block's keys between two waves of a workgroup.
  */
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          void* workspace, size_t workspace_bytes,

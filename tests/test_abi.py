@@ -207,20 +207,16 @@ def test_splitkv_plan():
     assert ws == 64 * 32 * 128 * 4 + 64 * 32 * 4
     assert binding.splitkv_workspace_size(1, 8, 2, 1, 40, 64, torch.bfloat16, 3) == 8 * 1 * 64 * 4 + 256
     assert binding.splitkv_workspace_size(1, 8, 3, 1, 40, 64, torch.bfloat16) == 0
-    # as many queries as keys (>= 128): key splits per query block; by default one at
-    # d = 128 (no workspace: the forward writes O and LSE itself), and at d = 64 two when
-    # fa_fwd's grid has at most 128 workgroups of 192 queries, else one; per row and split
-    # the fp32 part of O and its LSE
-    assert binding.splitkv_num_splits(1, 32, 8, 1024, 1024, 128) == 1      # 192 blocks
+    # as many queries as keys (>= 128): key splits per query block, one by default (no
+    # workspace: the forward writes O and LSE itself); per row and split the fp32 part of O
+    # and its LSE
+    for shape in ((1, 32, 8, 1024, 1024), (1, 16, 16, 1024, 1024), (1, 1, 1, 128, 128), (1, 4, 2, 4096, 4096)):
+        for d in (64, 128):
+            assert binding.splitkv_num_splits(*shape, d) == 1
     assert binding.splitkv_workspace_size(1, 32, 8, 1024, 1024, 128, torch.bfloat16) == 0
-    assert binding.splitkv_num_splits(1, 32, 8, 1024, 1024, 64) == 1       # 192 blocks
-    assert binding.splitkv_num_splits(1, 16, 16, 1024, 1024, 64) == 2      # 96 blocks
-    assert binding.splitkv_num_splits(1, 1, 1, 128, 128, 64) == 2          # one block of 2 tiles
-    assert binding.splitkv_num_splits(1, 4, 2, 4096, 4096, 64) == 2        # 88 blocks
-    assert binding.splitkv_num_splits(1, 4, 2, 4096, 4096, 128) == 1       # d = 128: always 1
-    assert binding.splitkv_num_splits(1, 1, 1, 128, 128, 128) == 1
     rows = 16 * 1024
-    assert binding.splitkv_workspace_size(1, 16, 16, 1024, 1024, 64, torch.bfloat16) == rows * 2 * (64 + 1) * 4
+    assert binding.splitkv_workspace_size(1, 16, 16, 1024, 1024, 64, torch.bfloat16) == 0
+    assert binding.splitkv_workspace_size(1, 16, 16, 1024, 1024, 64, torch.bfloat16, 2) == rows * 2 * (64 + 1) * 4
     rows = 32 * 1024
     # an explicit count: 5 splits of 16 tiles -> ceil(16/5) = 4 tiles each, 4 splits used
     ws5 = binding.splitkv_workspace_size(1, 32, 8, 1024, 1024, 128, torch.bfloat16, 5)
