@@ -180,6 +180,14 @@ def summarize(directory, pmc):
               f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f} |")
 
 
+def traffic_kind(substr: str) -> str:
+    """Which bench line a recorded kernel name (or '|'-separated names) belongs to."""
+    # the mask family runs fwd_unit_kernel with its general mode on (fifth template argument)
+    targs = substr[substr.find("<") + 1:substr.rfind(">")].split(", ") if "fwd_unit_kernel<" in substr else []
+    return ("decode" if ("splitkv" in substr or "combine" in substr) else "fp8" if "fp8" in substr
+            else "masks" if len(targs) >= 5 and targs[4] == "true" else "bwd" if "bwd" in substr else "fwd")
+
+
 def record_traffic(kdir, cdir, substr):
     # every kernel whose name contains substr runs once per call of the pass: sum them
     alts = substr.split("|")
@@ -193,10 +201,7 @@ def record_traffic(kdir, cdir, substr):
     kib = COPY_BYTES / 1024
     fetch_factor = kib / cc["FETCH_SIZE"] if cc.get("FETCH_SIZE") else None
     write_factor = kib / cc["WRITE_SIZE"] if cc.get("WRITE_SIZE") else None
-    # the mask family runs fwd_unit_kernel with its general mode on (fifth template argument)
-    targs = substr[substr.find("<") + 1:substr.rfind(">")].split(", ") if "fwd_unit_kernel<" in substr else []
-    kind = ("decode" if ("splitkv" in substr or "combine" in substr) else "fp8" if "fp8" in substr
-            else "masks" if len(targs) >= 5 and targs[4] == "true" else "bwd" if "bwd" in substr else "fwd")
+    kind = traffic_kind(substr)
     data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     data[kind] = {"kernel": kname, "source_hash": source_hash(kind),
                   "fetch_kib": kc.get("FETCH_SIZE"), "write_kib": kc.get("WRITE_SIZE"),
